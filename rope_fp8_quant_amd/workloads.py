@@ -1,0 +1,222 @@
+"""Seeded synthetic inputs for the DSA-indexer Q/K preparation.
+
+This module only draws inputs (numpy, host memory).  It holds none of the
+method's arithmetic, and it is the one piece of code that both the GPU path's
+tests/benchmark and the CPU oracle's tests use.
+
+Every array has its own random stream, spawned from ``SeedSequence(seed)`` in a
+fixed order: q, k, weights, positions, gamma, beta, slots, special structure.
+bf16 inputs are drawn in float32 and rounded to bf16 (nearest, ties to even)
+by bit arithmetic; they are returned as uint16 bit patterns.
+
+The five named workloads mirror the shapes the pages discuss: a 41-token
+decode (the size of the pages' K-cache writer comparison, 41 x 128 values),
+a 64-request decode batch, a 512-token decode batch with interleaved RoPE, an
+8192-token prefill chunk and a 65536-token prefill deep into a 262144-token
+context ([sglang-fuse] Accuracy and Benchmark; [vllm-47335] End-to-end).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ROW = 128          # head vector / K row width
+NEOX = 0
+INTERLEAVED = 1
+ROPE_BASE = 10000.0
+
+_STREAMS = ("q", "k", "weights", "positions", "gamma", "beta", "slots", "special")
+
+
+@dataclass
+class Workload:
+    name: str
+    T: int
+    H: int
+    rope_dim: int
+    style: int
+    q: np.ndarray            # uint16 bf16 bits [T, H, 128]
+    k: np.ndarray            # uint16 bf16 bits [T, 128]
+    weights: np.ndarray      # uint16 bf16 bits [T, H]
+    positions: np.ndarray    # int64 [T]
+    cos: np.ndarray          # float32 [P, rope_dim/2]
+    sin: np.ndarray          # float32 [P, rope_dim/2]
+    gamma: np.ndarray        # float32 [128]
+    beta: np.ndarray         # float32 [128]
+    eps: float
+    num_slots: int
+    out_cache_loc: np.ndarray  # int64 [T]
+    weight_scale: float = 1.0
+    info: dict = field(default_factory=dict)
+
+    @property
+    def table_rows(self) -> int:
+        return self.cos.shape[0]
+
+
+def f32_to_bf16_bits(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); finite inputs only."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for s in range(0, flat.size, chunk):
+        u = flat[s:s + chunk].view(np.uint32)
+        r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        out[s:s + chunk] = (r >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(x.shape)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def rope_table(rows: int, rope_dim: int = 64, base: float = ROPE_BASE):
+    """cos/sin [rows, rope_dim/2]: angle(p, j) = p * base^(-2j/rope_dim) in
+    float64, each rounded to float32.  The table is an input of the method."""
+    j = np.arange(rope_dim // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / rope_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _rngs(seed):
+    kids = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    return {name: np.random.default_rng(s) for name, s in zip(_STREAMS, kids)}
+
+
+def _draw_values(rng, shape, values, chunk_rows=2048):
+    """Draw float32 values row-chunk by row-chunk (first axis) and round to bf16."""
+    out = np.empty(shape, dtype=np.uint16)
+    n0 = shape[0]
+    for s in range(0, n0, chunk_rows):
+        sub = (min(chunk_rows, n0 - s),) + tuple(shape[1:])
+        if values == "student_t3":
+            v = rng.standard_t(3, size=sub).astype(np.float32)
+        else:
+            v = rng.standard_normal(sub, dtype=np.float32)
+        out[s:s + sub[0]] = f32_to_bf16_bits(v)
+    return out
+
+
+def make(T: int, H: int = 64, *, rope_dim: int = 64, style: int = NEOX,
+         values: str = "normal", table_rows: int = 4096, pos_mode: str = "uniform",
+         pos_lo: int = 0, pos_hi: int | None = None, num_slots: int = 4096,
+         slot_mode: str = "random_distinct", seed: int = 0, name: str = "custom",
+         eps: float = 1e-6) -> Workload:
+    """Build a workload.
+
+    values: "normal" N(0,1); "student_t3"; "outlier_channels" (N(0,1), channels
+      3 and 77 of every head and of k times 20); "sparse_outliers" (N(0,1) with
+      each entry times 50 with probability 0.01); "zero_rows" (N(0,1) with
+      round(0.001 * rows) Q rows and K rows set to zero).
+    pos_mode: "uniform" ints in [pos_lo, pos_hi); "contiguous" pos_lo + t.
+    slot_mode: "perm_prefix" first T of a permutation of the slots;
+      "random_distinct"; "contiguous" (block at a random offset).
+    """
+    if pos_hi is None:
+        pos_hi = table_rows
+    r = _rngs(seed)
+    base_values = "student_t3" if values == "student_t3" else "normal"
+    q_bits = _draw_values(r["q"], (T, H, ROW), base_values)
+    k_bits = _draw_values(r["k"], (T, ROW), base_values)
+    w_bits = f32_to_bf16_bits(r["weights"].standard_normal((T, H), dtype=np.float32))
+    if pos_mode == "contiguous":
+        positions = pos_lo + np.arange(T, dtype=np.int64)
+    else:
+        positions = r["positions"].integers(pos_lo, pos_hi, size=T, dtype=np.int64)
+    gamma = (1.0 + 0.1 * r["gamma"].standard_normal(ROW)).astype(np.float32)
+    beta = (0.1 * r["beta"].standard_normal(ROW)).astype(np.float32)
+    rs = r["slots"]
+    if slot_mode == "perm_prefix":
+        loc = rs.permutation(num_slots)[:T].astype(np.int64)
+    elif slot_mode == "contiguous":
+        off = int(rs.integers(0, num_slots - T + 1))
+        loc = off + np.arange(T, dtype=np.int64)
+    else:
+        loc = rs.choice(num_slots, size=T, replace=False).astype(np.int64)
+
+    info = {}
+    sp = r["special"]
+    if values == "outlier_channels":
+        for ch in (3, 77):
+            qf = bf16_bits_to_f32(q_bits[:, :, ch]) * np.float32(20.0)
+            q_bits[:, :, ch] = f32_to_bf16_bits(qf)
+            kf = bf16_bits_to_f32(k_bits[:, ch]) * np.float32(20.0)
+            k_bits[:, ch] = f32_to_bf16_bits(kf)
+    elif values == "sparse_outliers":
+        for arr in (q_bits, k_bits):
+            flat = arr.reshape(-1)
+            mask = sp.random(flat.size) < 0.01
+            idx = np.nonzero(mask)[0]
+            flat[idx] = f32_to_bf16_bits(bf16_bits_to_f32(flat[idx]) * np.float32(50.0))
+        info["outlier_scale"] = 50.0
+    elif values == "zero_rows":
+        nq = int(round(0.001 * T * H))
+        nk = int(round(0.001 * T))
+        zq = np.sort(sp.choice(T * H, size=nq, replace=False)) if nq else np.zeros(0, np.int64)
+        zk = np.sort(sp.choice(T, size=nk, replace=False)) if nk else np.zeros(0, np.int64)
+        q_bits.reshape(T * H, ROW)[zq] = 0
+        k_bits[zk] = 0
+        info["zero_q_rows"] = zq.astype(np.int64)
+        info["zero_k_rows"] = zk.astype(np.int64)
+
+    cos, sin = rope_table(table_rows, rope_dim)
+    return Workload(name=name, T=T, H=H, rope_dim=rope_dim, style=style, q=q_bits, k=k_bits,
+                    weights=w_bits, positions=positions, cos=cos, sin=sin, gamma=gamma,
+                    beta=beta, eps=eps, num_slots=num_slots, out_cache_loc=loc, info=info)
+
+
+# The five named workloads.  Index -> (name, keyword arguments of make()).
+NAMED = [
+    ("decode_tiny_T41", dict(T=41, values="outlier_channels", table_rows=4096,
+                             num_slots=4096, slot_mode="perm_prefix")),
+    ("decode_batch_T64", dict(T=64, values="sparse_outliers", table_rows=8192,
+                              num_slots=65536, slot_mode="random_distinct")),
+    ("decode_large_interleaved_T512", dict(T=512, style=INTERLEAVED, values="normal",
+                                           table_rows=131072, num_slots=262144,
+                                           slot_mode="random_distinct")),
+    ("prefill_chunk_T8192", dict(T=8192, values="student_t3", table_rows=8192,
+                                 pos_mode="contiguous", pos_lo=0, num_slots=262144,
+                                 slot_mode="contiguous")),
+    ("long_prefill_T65536", dict(T=65536, values="zero_rows", table_rows=262144,
+                                 pos_mode="contiguous", pos_lo=196608, num_slots=262144,
+                                 slot_mode="contiguous")),
+]
+
+
+def named(idx: int, T: int | None = None) -> Workload:
+    """Named workload idx (seed 1000 + idx).  T overrides the token count for
+    a smaller instance of the same recipe (positions and slots re-drawn)."""
+    name, kw = NAMED[idx]
+    kw = dict(kw)
+    if T is not None:
+        kw["T"] = T
+        if kw.get("pos_mode") == "contiguous":
+            kw["pos_lo"] = min(kw.get("pos_lo", 0), kw["table_rows"] - T)
+    return make(seed=1000 + idx, name=name, **kw)
+
+
+def bytes_per_token(H: int = 64, entry: str = "fused", rope_dim: int = 64,
+                    q_scale_out: bool = False) -> int:
+    """Algorithmic HBM bytes per token: each input read once, each output
+    written once; the cos/sin row is counted once per token, not per head."""
+    cos_sin = 2 * (rope_dim // 2) * 4
+    # q bf16 + weights bf16 + position + cos/sin + q_fp8 + weights_out (fp32)
+    q_side = H * ROW * 2 + H * 2 + 8 + cos_sin + H * ROW + H * 4
+    if q_scale_out:
+        q_side += H * 4
+    # k bf16 + position + slot + fp8 row + fp32 scale
+    k_side = ROW * 2 + 8 + 8 + ROW + 4
+    if entry == "q":
+        return q_side
+    if entry == "k":
+        return k_side + cos_sin
+    return q_side + k_side - 8   # fused: the position is read once per token
+
+
+def bytes_per_call(T: int, H: int = 64, entry: str = "fused", rope_dim: int = 64) -> int:
+    """bytes_per_token * T, plus the LayerNorm gamma and beta (fp32 [128] each)
+    once per call for the entries that run K rows."""
+    per_call = 0 if entry == "q" else 2 * ROW * 4
+    return T * bytes_per_token(H, entry, rope_dim) + per_call
