@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Throughput of the fused DSA-indexer Q/K preparation on one MI355X.
+
+One step = one dsaidx_qk_fused call over the whole long-prefill batch
+(T = 65536 tokens at positions 196608..262143, H = 64 heads, D = 128,
+rope_dim 64 NeoX, cos/sin table of 262144 rows, 262144-slot index-K cache,
+contiguous slots): query RoPE + E4M3FN/ue8m0 quantisation + head-gate fold
+and key LayerNorm + RoPE + quantisation + cache store, in one dispatch.
+Inputs are resident in HBM before timing starts; the 1.68 GB a step moves is
+far larger than the 256 MB last-level cache, so every step streams from HBM.
+
+Printed: one JSON line with tokens/s (value), ms per step, the HBM roofline
+of the kernel (algorithmic bytes / measured launch time against 8 TB/s), the
+oracle's CPU throughput on a bounded sample, and secondary measurements
+(decode-batch microseconds per call, the 8192-token prefill chunk with buffer
+rotation, the k-only decode path, a plain-copy bandwidth reference).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", f)
+                  for f in ("dsaidx_kernels.hip", "dsaidx_internal.h", "dsaidx_api.cpp")]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_indexer_qk_prep_long_prefill_T65536.txt")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(expected_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m_hash = re.search(r"^kernel_source_sha256_16:\s*([0-9a-f]+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != expected_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+class Case:
+    """Device buffers of one workload for the fused call (inputs copied once)."""
+
+    def __init__(self, wl, torch, R):
+        import numpy as np
+        self.wl = wl
+        T, H = wl.T, wl.H
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+        self.q, self.k, self.w = bf16(wl.q), bf16(wl.k), bf16(wl.weights)
+        self.pos = torch.from_numpy(wl.positions).cuda()
+        self.loc = torch.from_numpy(wl.out_cache_loc).cuda()
+        self.cos = torch.from_numpy(wl.cos).cuda()
+        self.sin = torch.from_numpy(wl.sin).cuda()
+        self.gamma = torch.from_numpy(wl.gamma).cuda()
+        self.beta = torch.from_numpy(wl.beta).cuda()
+        self.q_fp8 = torch.empty((T, H, 128), dtype=torch.uint8, device="cuda")
+        self.w_out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        self.k_cache = torch.zeros((wl.num_slots, 128), dtype=torch.uint8, device="cuda")
+        self.k_scale = torch.zeros((wl.num_slots,), dtype=torch.float32, device="cuda")
+        self.qa = R.q_args(self.q, self.w, self.pos, self.q_fp8, self.w_out)
+        self.ka = R.k_args(self.k, self.gamma, self.beta, wl.eps, self.pos, self.loc,
+                           self.k_cache, self.k_scale)
+        self.rope = R.rope_args(self.cos, self.sin, wl.rope_dim, wl.style)
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Mean milliseconds per call over `steps` back-to-back calls, bracketed by
+    HIP events on the stream the calls are enqueued on."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_graph(torch, fn, calls, replays):
+    """Mean milliseconds per call when `calls` calls are captured in one HIP
+    graph and the graph is replayed `replays` times."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (calls * replays)
+
+
+def cpu_baseline(wl, target_s=5.0):
+    """The oracle (as it stands) on a leading slice of the workload, all
+    allowed host cores, sized to roughly target_s seconds of wall time."""
+    import numpy as np
+
+    import oracle
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    kc = np.zeros((wl.num_slots, 128), np.uint8)
+    ks = np.zeros(wl.num_slots, np.float32)
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.q_side(wl.q[:n], wl.weights[:n], wl.positions[:n], wl.cos, wl.sin, wl.rope_dim,
+                      wl.style, wl.weight_scale, nthreads=cores)
+        oracle.k_side(wl.k[:n], wl.gamma, wl.beta, wl.eps, wl.positions[:n],
+                      wl.out_cache_loc[:n], wl.cos, wl.sin, kc, ks, wl.rope_dim, wl.style,
+                      nthreads=cores)
+        return time.perf_counter() - t0
+
+    n0 = min(wl.T, 512)
+    dt = run(n0)
+    n = int(min(wl.T, max(n0, n0 * target_s / max(dt, 1e-6))))
+    dt = run(n)
+    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample="first %d of %d tokens of %s (Q and K sides), one pass, %.2f s wall"
+                       % (n, wl.T, wl.name, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary measurements (decode, prefill chunk, k-only, copy)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path has no cross-GPU step (every token and "
+              "head is independent), and only --gpus 1 is supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rope_fp8_quant_amd as R
+    from rope_fp8_quant_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    if not R.dsaidx_device_supported(0):
+        raise SystemExit("cuda:0 is not a gfx950 device")
+
+    log("generating long_prefill_T65536 inputs")
+    wl = W.named(4)
+    c = Case(wl, torch, R)
+    bytes_call = W.bytes_per_call(wl.T, wl.H, "fused", wl.rope_dim)
+
+    def fused():
+        R.dsaidx_qk_fused(c.qa, c.ka, c.rope)
+
+    log("timing %d fused steps after %d warmup" % (args.steps, args.warmup))
+    torch.cuda.synchronize()
+    ms = time_calls(torch, fused, args.steps, args.warmup)
+    achieved = bytes_call / (ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = recorded_traffic(src_hash)
+    result = {
+        "metric": "fused indexer Q/K prep tokens/s and achieved HBM GB/s (% peak); us/call",
+        "value": wl.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "D": 128,
+                   "rope_dim": wl.rope_dim, "rope_style": "neox", "positions": "196608..262143",
+                   "table_rows": wl.table_rows, "cache_slots": wl.num_slots,
+                   "entry": "dsaidx_qk_fused", "inputs": "bf16 q/k/weights",
+                   "outputs": "e4m3fn codes + fp32 scales/weights",
+                   "algorithmic_bytes_per_step": bytes_call},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic, "kernel_source_sha256_16": src_hash},
+        "us_per_call": ms * 1e3,
+    }
+    del c
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        extras = {}
+        # decode batch, 64 tokens: back-to-back calls and graph replay
+        wl1 = W.named(1)
+        c1 = Case(wl1, torch, R)
+
+        def fused1():
+            R.dsaidx_qk_fused(c1.qa, c1.ka, c1.rope)
+
+        ms_eager = time_calls(torch, fused1, 2000, 200)
+        ms_graph = time_graph(torch, fused1, 100, 20)
+        extras["decode_batch_T64"] = {"us_per_call_eager": ms_eager * 1e3,
+                                      "us_per_call_graph": ms_graph * 1e3,
+                                      "bytes_per_call": W.bytes_per_call(64)}
+        # 512-token decode, interleaved RoPE: fused and k-only
+        wl2 = W.named(2)
+        c2 = Case(wl2, torch, R)
+        ms2 = time_graph(torch, lambda: R.dsaidx_qk_fused(c2.qa, c2.ka, c2.rope), 100, 10)
+        ms2k = time_graph(torch, lambda: R.dsaidx_k_only_prepare_store(c2.ka, c2.rope), 100, 10)
+        extras["decode_large_interleaved_T512"] = {"us_per_call_fused_graph": ms2 * 1e3,
+                                                   "us_per_call_k_only_graph": ms2k * 1e3}
+        del c1, c2
+        # 8192-token prefill chunk: 4 rotating buffer sets (> 800 MB) so no
+        # step finds its inputs in the last-level cache
+        wl3 = W.named(3)
+        sets = [Case(wl3, torch, R) for _ in range(4)]
+        it = [0]
+
+        def fused3():
+            s = sets[it[0] & 3]
+            it[0] += 1
+            R.dsaidx_qk_fused(s.qa, s.ka, s.rope)
+
+        ms3 = time_calls(torch, fused3, 200, 20)
+        b3 = W.bytes_per_call(wl3.T)
+        extras["prefill_chunk_T8192"] = {"us_per_call": ms3 * 1e3, "tokens_per_s": wl3.T / (ms3 * 1e-3),
+                                         "achieved_GBps": b3 / (ms3 * 1e-3) / 1e9,
+                                         "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del sets
+        torch.cuda.empty_cache()
+        # plain device copy of the same byte count (reference for the achievable bandwidth)
+        n = bytes_call // 2
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        msc = time_calls(torch, lambda: dst.copy_(src), 50, 5)
+        extras["plain_copy"] = {"bytes_moved": 2 * n, "achieved_GBps": 2 * n / (msc * 1e-3) / 1e9}
+        result["roofline"]["frac_of_plain_copy"] = achieved / extras["plain_copy"]["achieved_GBps"]
+        del src, dst
+        result["secondary"] = extras
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,225 @@
+/*
+ * libdsaidx — DSA-indexer Q/K preparation on MI355X (gfx950).
+ *
+ * The DeepSeek-Sparse-Attention indexer prepares its query and key before
+ * scoring.  Query side, per (token t, head h): RoPE on the rope slice of the
+ * 128-wide head vector, quantisation of the vector to FP8 E4M3FN with one
+ * power-of-two (ue8m0) scale, and the scale folded into the head-gate weight.
+ * Key side, per token: fp32 LayerNorm with fp32 affine parameters, the same
+ * RoPE and quantisation, and a scatter of the fp8 row and its scale into the
+ * slot-indexed index-K cache at out_cache_loc[t].
+ *
+ * Sources (page title and section):
+ *   [sglang-fuse] sglang PR "[AMD] [GLM5] Fuse the DSA indexer Q/K rope + quant
+ *     + K-cache write": Motivation (the operations and their single-launch
+ *     fusion), Modifications (the (q_fp8, weights) result sliced to num_tokens,
+ *     fp32 norm parameters, separate cos/sin tables, the k-only store path, the
+ *     sliced out_cache_loc), Accuracy (ue8m0 scales, one fp32 -> fp8 step),
+ *     Profile (one launch instead of four), Checklist (strided inputs, a
+ *     replaced rope table, both cache writers).
+ *   [vllm-47335] vLLM PR 47335 "[ROCm][Perf] Enable fused indexer-Q RoPE+quant
+ *     kernel for DeepSeek/GLM sparse attention": Summary (query RoPE + FP8
+ *     quantisation + weight-scale fold in one launch), Kernel-level evidence.
+ *
+ * Numerics (every entry point, bit for bit the same per row):
+ *   x          = fp32(bf16 input)                       (exact)
+ *   K only:    mu = fp32(sum x / 128), var = fp32(sum (x - mu)^2 / 128)
+ *              with fp64 sums, r = fp32(1 / sqrt(fp64 var + fp64 eps)),
+ *              n_i = ((x_i - mu) * r) * gamma_i + beta_i  (each op rounded)
+ *   RoPE       pair (a, b) -> (a*c - b*s, b*c + a*s) with c, s = cos/sin of
+ *              table row positions[t], column i for pair i < rope_dim/2;
+ *              NeoX pairs (i, i + rope_dim/2), interleaved pairs (2i, 2i+1);
+ *              elements >= rope_dim pass through.  No fused multiply-add.
+ *   scale      e = smallest integer with max(amax, 1e-4) <= 448 * 2^e, where
+ *              amax = max |y| over the 128 values (1e-4 is the zero-row guard)
+ *   codes      E4M3FN(y * 2^-e), round to nearest even; |y * 2^-e| <= 448 by
+ *              construction, so no value saturates
+ *   Q extra    weights_out = (fp32(w) * weight_scale) * 2^e; q_scale_out = 2^e
+ *   K extra    k_cache[slot][0..127] = codes, k_scale[slot] = 2^e
+ *
+ * Ownership and execution: every pointer is caller-owned DEVICE memory except
+ * the argument structs themselves (host memory, read during the call only).
+ * The library allocates nothing, keeps no per-call state and caches no data,
+ * so a replaced or rewritten rope table is always honoured.  Work is enqueued
+ * asynchronously on `stream` (a hipStream_t; NULL = the null stream of the
+ * current device) as exactly one kernel dispatch per call, with no host
+ * synchronisation, no device-to-host reads and no memsets, so calls can be
+ * captured in a HIP graph.  Calls are reentrant and thread-safe.
+ *
+ * Errors: all arguments are checked on the host before anything is enqueued;
+ * a failed check returns DSAIDX_ERR_INVALID_ARGUMENT and enqueues nothing.
+ * num_tokens == 0 (on both sides for the fused call) returns DSAIDX_OK without
+ * a launch and without looking at the pointers, since graph split-op slices
+ * may be empty and empty tensors may have NULL data pointers.  A launch the HIP runtime rejects returns
+ * DSAIDX_ERR_UNSUPPORTED (no gfx950 device / no code object for it) or
+ * DSAIDX_ERR_HIP.  Kernel execution errors surface on the stream as usual.
+ *
+ * Preconditions that are not checked (device data is never read on the host):
+ *   - positions[t] in [0, max_position).  A position outside is clamped to the
+ *     table for the read, so no access leaves the table; the output of that
+ *     token is then unspecified.
+ *   - out_cache_loc entries are distinct (repeated slots race).  Entries < 0 or
+ *     >= num_slots are skipped: nothing is written for that token.
+ *   - inputs are finite with |x| < 2^100; outputs do not overlap inputs or
+ *     each other.
+ */
+#ifndef DSAIDX_H
+#define DSAIDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSAIDX_ABI_VERSION 1
+#define DSAIDX_HEAD_DIM 128 /* width of every head vector and K row */
+
+typedef struct ihipStream_t* dsaidx_stream_t; /* the same type as hipStream_t */
+
+typedef enum dsaidx_status {
+    DSAIDX_OK = 0,
+    DSAIDX_ERR_INVALID_ARGUMENT = 1,
+    DSAIDX_ERR_UNSUPPORTED = 2,
+    DSAIDX_ERR_HIP = 3
+} dsaidx_status;
+
+typedef enum dsaidx_rope_style {
+    DSAIDX_ROPE_NEOX = 0,       /* pairs (i, i + rope_dim/2) */
+    DSAIDX_ROPE_INTERLEAVED = 1 /* pairs (2i, 2i + 1) */
+} dsaidx_rope_style;
+
+/* RoPE tables, read by token position ([sglang-fuse] Modifications: cos and
+ * sin are kept as two tables of rope_dim/2 columns).  Row p of the cosine
+ * table starts at cos + p * row_stride; likewise sin.  A single combined
+ * cos_sin cache of [P, rope_dim] floats is passed as cos = cache,
+ * sin = cache + rope_dim/2, row_stride = rope_dim.
+ *   cos, sin      fp32, 16-byte aligned
+ *   row_stride    floats between rows; >= rope_dim/2 and a multiple of 4
+ *   max_position  number of table rows P >= 1
+ *   rope_dim      rotated leading dims; a multiple of 16 in [16, 128]
+ *   style         dsaidx_rope_style */
+typedef struct dsaidx_rope {
+    const float* cos;
+    const float* sin;
+    int64_t row_stride;
+    int64_t max_position;
+    int32_t rope_dim;
+    int32_t style;
+} dsaidx_rope;
+
+/* Query side ([sglang-fuse] Modifications: the (q_fp8, weights) result;
+ * [vllm-47335] Summary).  Strides are in elements.
+ *   q            bf16 bits [T, H, 128]: (t, h, i) at q[t*q_stride_t + h*q_stride_h + i];
+ *                16-byte aligned; q_stride_h >= 128 and q_stride_t >= (H-1)*q_stride_h + 128,
+ *                both multiples of 8 (padded head strides are allowed)
+ *   weights      bf16 bits head gates [T, H]: (t, h) at weights[t*w_stride_t + h];
+ *                w_stride_t >= H (a column slice of a wider GEMM output is allowed)
+ *   positions    int64 [T], 8-byte aligned
+ *   num_tokens   T >= 0
+ *   num_heads    H in [1, 4096]
+ *   weight_scale finite constant folded into every gate (1.0 for none)
+ *   q_fp8        out: E4M3FN [T, H, 128] contiguous, 8-byte aligned
+ *   weights_out  out: fp32 [T, H] contiguous, 4-byte aligned
+ *   q_scale_out  out: fp32 [T, H] contiguous (2^e per row), or NULL */
+typedef struct dsaidx_q_args {
+    const uint16_t* q;
+    int64_t q_stride_t;
+    int64_t q_stride_h;
+    const uint16_t* weights;
+    int64_t w_stride_t;
+    const int64_t* positions;
+    int64_t num_tokens;
+    int32_t num_heads;
+    float weight_scale;
+    uint8_t* q_fp8;
+    float* weights_out;
+    float* q_scale_out;
+} dsaidx_q_args;
+
+/* Key side ([sglang-fuse] Motivation and Modifications: fp32 LayerNorm with
+ * fp32 params, the index-K cache write at the sliced out_cache_loc).
+ *   k                  bf16 bits [T, 128]: row t at k + t*k_stride_t; 16-byte aligned;
+ *                      k_stride_t >= 128 and a multiple of 8 (a column slice of a
+ *                      wider GEMM output is allowed)
+ *   ln_gamma, ln_beta  fp32 [128], 16-byte aligned
+ *   ln_eps             > 0, finite
+ *   flags              must be 0 (reserved)
+ *   positions          int64 [T], 8-byte aligned
+ *   out_cache_loc      int64 [T] slot per token, 8-byte aligned
+ *   num_tokens         T >= 0
+ *   k_cache            in/out: E4M3FN rows; slot s at k_cache + s*k_cache_row_stride,
+ *                      codes in its first 128 bytes; 8-byte aligned
+ *   k_cache_row_stride bytes, >= 128 and a multiple of 8
+ *   k_scale            in/out: fp32 [num_slots], 4-byte aligned
+ *   num_slots          S >= 1 */
+typedef struct dsaidx_k_args {
+    const uint16_t* k;
+    int64_t k_stride_t;
+    const float* ln_gamma;
+    const float* ln_beta;
+    float ln_eps;
+    int32_t flags;
+    const int64_t* positions;
+    const int64_t* out_cache_loc;
+    int64_t num_tokens;
+    uint8_t* k_cache;
+    int64_t k_cache_row_stride;
+    float* k_scale;
+    int64_t num_slots;
+} dsaidx_k_args;
+
+/* Query RoPE + fp8/ue8m0 quantisation + head-gate fold: the fused-Q launch of
+ * [vllm-47335] Summary.  One dispatch over the T*H head vectors. */
+dsaidx_status dsaidx_q_rope_quant_fold(const dsaidx_q_args* q, const dsaidx_rope* rope,
+                                       dsaidx_stream_t stream);
+
+/* Key LayerNorm + RoPE + quantisation + index-K cache store: the key half of
+ * the fused-Q tier, where the key path stays a launch of its own
+ * ([vllm-47335] Kernel-level evidence).  One dispatch over the T key rows. */
+dsaidx_status dsaidx_k_norm_rope_quant_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
+                                             dsaidx_stream_t stream);
+
+/* The whole Q and K preparation in ONE dispatch ([sglang-fuse] Motivation and
+ * Profile: four launches per layer become one).  q->num_tokens must equal
+ * k->num_tokens; Q rows read q->positions and K rows k->positions (normally
+ * the same array).  Outputs are byte-identical to dsaidx_q_rope_quant_fold
+ * followed by dsaidx_k_norm_rope_quant_store. */
+dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
+                              const dsaidx_rope* rope, dsaidx_stream_t stream);
+
+/* K-only prepare-and-store for the dense decode fast path that skips the
+ * indexer while the KV length is within index_topk ([sglang-fuse]
+ * Modifications and Benchmark).  Same arithmetic and bytes as
+ * dsaidx_k_norm_rope_quant_store; a launch shape for few tokens. */
+dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
+                                          dsaidx_stream_t stream);
+
+/* Encode n fp32 values to E4M3FN bytes with the device conversion every
+ * kernel above uses (round to nearest even), so the conversion can be checked
+ * on its own against the format definition.  in: device fp32 [n], 4-byte
+ * aligned, every value in [-448, 448] (values outside are outside the
+ * contract); out: device bytes [n], 8-byte aligned; n >= 0.  One dispatch. */
+dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,
+                                         dsaidx_stream_t stream);
+
+/* 1 if `device` is a gfx950 GPU this library has code for, else 0 (also when
+ * no GPU or HIP runtime is present).  The counterpart of the import-time
+ * kernel probe of [sglang-fuse] Modifications. */
+int dsaidx_device_supported(int device);
+
+/* Static, never-NULL description of a status code. */
+const char* dsaidx_status_string(dsaidx_status status);
+
+/* DSAIDX_ABI_VERSION of the built library. */
+int dsaidx_abi_version(void);
+
+/* sizeof the argument structs as built (0 = dsaidx_rope, 1 = dsaidx_q_args,
+ * 2 = dsaidx_k_args; anything else returns 0), for binding checks. */
+size_t dsaidx_struct_size(int which);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSAIDX_H */

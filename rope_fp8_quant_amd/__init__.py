@@ -1,0 +1,30 @@
+"""rope_fp8_quant_amd — the DSA-indexer Q/K preparation on MI355X (gfx950).
+
+The computation lives in libdsaidx.so (hand-written HIP kernels behind a C ABI,
+declared in include/dsaidx.h).  This package is its thin binding plus the
+seeded synthetic workloads used to test and benchmark it.
+"""
+from .binding import (  # noqa: F401
+    DSAIDX_ERR_HIP,
+    DSAIDX_ERR_INVALID_ARGUMENT,
+    DSAIDX_ERR_UNSUPPORTED,
+    DSAIDX_OK,
+    DSAIDX_ROPE_INTERLEAVED,
+    DSAIDX_ROPE_NEOX,
+    DsaidxError,
+    DsaidxKArgs,
+    DsaidxQArgs,
+    DsaidxRope,
+    dsaidx_abi_version,
+    dsaidx_device_supported,
+    dsaidx_fp8_encode_selftest,
+    dsaidx_k_norm_rope_quant_store,
+    dsaidx_k_only_prepare_store,
+    dsaidx_q_rope_quant_fold,
+    dsaidx_qk_fused,
+    dsaidx_status_string,
+    k_args,
+    lib,
+    q_args,
+    rope_args,
+)

@@ -1,0 +1,235 @@
+"""Thin ctypes binding of libdsaidx (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+fills the C argument structs from torch tensors (device pointers and strides)
+and calls the entry points of the same names.  torch is used for device memory
+and streams only.  There is no fallback: if libdsaidx.so is missing or the
+device is not supported, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdsaidx.so")
+ROW = 128
+
+DSAIDX_OK = 0
+DSAIDX_ERR_INVALID_ARGUMENT = 1
+DSAIDX_ERR_UNSUPPORTED = 2
+DSAIDX_ERR_HIP = 3
+DSAIDX_ROPE_NEOX = 0
+DSAIDX_ROPE_INTERLEAVED = 1
+EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaidx_qk_fused",
+            "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
+            "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest")
+
+
+class DsaidxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, status_string(status)))
+
+
+class DsaidxRope(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
+                ("row_stride", ctypes.c_int64), ("max_position", ctypes.c_int64),
+                ("rope_dim", ctypes.c_int32), ("style", ctypes.c_int32)]
+
+
+class DsaidxQArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_stride_t", ctypes.c_int64),
+                ("q_stride_h", ctypes.c_int64), ("weights", ctypes.c_void_p),
+                ("w_stride_t", ctypes.c_int64), ("positions", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int32),
+                ("weight_scale", ctypes.c_float), ("q_fp8", ctypes.c_void_p),
+                ("weights_out", ctypes.c_void_p), ("q_scale_out", ctypes.c_void_p)]
+
+
+class DsaidxKArgs(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("k_stride_t", ctypes.c_int64),
+                ("ln_gamma", ctypes.c_void_p), ("ln_beta", ctypes.c_void_p),
+                ("ln_eps", ctypes.c_float), ("flags", ctypes.c_int32),
+                ("positions", ctypes.c_void_p), ("out_cache_loc", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_int64), ("k_cache", ctypes.c_void_p),
+                ("k_cache_row_stride", ctypes.c_int64), ("k_scale", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsaidx.so (built in-tree by rope_fp8_quant_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libdsaidx.so is not built (%s); run "
+                               "`python -m rope_fp8_quant_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        for name, args in (("dsaidx_q_rope_quant_fold", [ctypes.POINTER(DsaidxQArgs),
+                                                         ctypes.POINTER(DsaidxRope), P]),
+                           ("dsaidx_k_norm_rope_quant_store", [ctypes.POINTER(DsaidxKArgs),
+                                                               ctypes.POINTER(DsaidxRope), P]),
+                           ("dsaidx_k_only_prepare_store", [ctypes.POINTER(DsaidxKArgs),
+                                                            ctypes.POINTER(DsaidxRope), P]),
+                           ("dsaidx_qk_fused", [ctypes.POINTER(DsaidxQArgs),
+                                                ctypes.POINTER(DsaidxKArgs),
+                                                ctypes.POINTER(DsaidxRope), P])):
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.dsaidx_fp8_encode_selftest.argtypes = [P, P, ctypes.c_int64, P]
+        L.dsaidx_fp8_encode_selftest.restype = ctypes.c_int
+        L.dsaidx_device_supported.argtypes = [ctypes.c_int]
+        L.dsaidx_device_supported.restype = ctypes.c_int
+        L.dsaidx_status_string.argtypes = [ctypes.c_int]
+        L.dsaidx_status_string.restype = ctypes.c_char_p
+        L.dsaidx_abi_version.argtypes = []
+        L.dsaidx_abi_version.restype = ctypes.c_int
+        L.dsaidx_struct_size.argtypes = [ctypes.c_int]
+        L.dsaidx_struct_size.restype = ctypes.c_size_t
+        for which, cls in enumerate((DsaidxRope, DsaidxQArgs, DsaidxKArgs)):
+            if L.dsaidx_struct_size(which) != ctypes.sizeof(cls):
+                raise RuntimeError("libdsaidx ABI mismatch for %s" % cls.__name__)
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().dsaidx_status_string(int(status)).decode()
+
+
+def dsaidx_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def dsaidx_device_supported(device: int = 0) -> bool:
+    return bool(lib().dsaidx_device_supported(int(device)))
+
+
+def dsaidx_abi_version() -> int:
+    return int(lib().dsaidx_abi_version())
+
+
+# ------------------------------------------------------ stream handling ----
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != DSAIDX_OK:
+        raise DsaidxError(status, where)
+
+
+# -------------------------------------------------------- entry points ----
+
+def dsaidx_q_rope_quant_fold(q: DsaidxQArgs, rope: DsaidxRope, stream=None) -> None:
+    _check(lib().dsaidx_q_rope_quant_fold(ctypes.byref(q), ctypes.byref(rope),
+                                          _stream_handle(stream)), "dsaidx_q_rope_quant_fold")
+
+
+def dsaidx_k_norm_rope_quant_store(k: DsaidxKArgs, rope: DsaidxRope, stream=None) -> None:
+    _check(lib().dsaidx_k_norm_rope_quant_store(ctypes.byref(k), ctypes.byref(rope),
+                                                _stream_handle(stream)),
+           "dsaidx_k_norm_rope_quant_store")
+
+
+def dsaidx_qk_fused(q: DsaidxQArgs, k: DsaidxKArgs, rope: DsaidxRope, stream=None) -> None:
+    _check(lib().dsaidx_qk_fused(ctypes.byref(q), ctypes.byref(k), ctypes.byref(rope),
+                                 _stream_handle(stream)), "dsaidx_qk_fused")
+
+
+def dsaidx_k_only_prepare_store(k: DsaidxKArgs, rope: DsaidxRope, stream=None) -> None:
+    _check(lib().dsaidx_k_only_prepare_store(ctypes.byref(k), ctypes.byref(rope),
+                                             _stream_handle(stream)), "dsaidx_k_only_prepare_store")
+
+
+def dsaidx_fp8_encode_selftest(inp, out, stream=None) -> None:
+    """inp: float32 device tensor (contiguous, values in [-448, 448]); out: 1-byte
+    device tensor with as many elements."""
+    _need(inp.is_contiguous() and out.is_contiguous() and inp.numel() == out.numel()
+          and out.element_size() == 1, "contiguous float32 input and 1-byte output of equal size")
+    _check(lib().dsaidx_fp8_encode_selftest(ctypes.c_void_p(_ptr(inp)), ctypes.c_void_p(_ptr(out)),
+                                            inp.numel(), _stream_handle(stream)),
+           "dsaidx_fp8_encode_selftest")
+
+
+# ------------------------------------------- struct builders from tensors ----
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def rope_args(cos, sin, rope_dim: int = 64, style: int = DSAIDX_ROPE_NEOX) -> DsaidxRope:
+    """cos, sin: float32 [P, >= rope_dim/2] views with unit column stride and
+    a common row stride (e.g. the two halves of one [P, rope_dim] cache)."""
+    import torch
+    _need(cos.dtype == torch.float32 and sin.dtype == torch.float32, "cos/sin must be float32")
+    _need(cos.dim() == 2 and sin.dim() == 2 and cos.shape[0] == sin.shape[0], "cos/sin [P, n]")
+    _need(cos.stride(1) == 1 and sin.stride(1) == 1 and cos.stride(0) == sin.stride(0),
+          "cos/sin need unit column stride and one row stride")
+    return DsaidxRope(_ptr(cos), _ptr(sin), cos.stride(0), cos.shape[0], rope_dim, style)
+
+
+def q_args(q, weights, positions, q_fp8, weights_out, q_scale_out=None,
+           weight_scale: float = 1.0) -> DsaidxQArgs:
+    """q: bf16 [T, H, 128] (unit inner stride); weights: bf16 [T, H] (unit
+    inner stride); positions int64 [T]; q_fp8 uint8 or float8_e4m3fn
+    [T, H, 128] contiguous; weights_out (and q_scale_out) float32 [T, H]
+    contiguous."""
+    import torch
+    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == ROW and q.stride(2) == 1,
+          "q must be bf16 [T, H, 128] with unit inner stride")
+    T, H = q.shape[0], q.shape[1]
+    _need(weights.dtype == torch.bfloat16 and tuple(weights.shape) == (T, H)
+          and weights.stride(1) == 1, "weights must be bf16 [T, H] with unit inner stride")
+    _need(positions.dtype == torch.int64 and positions.numel() == T and positions.is_contiguous(),
+          "positions must be contiguous int64 [T]")
+    _need(q_fp8.element_size() == 1 and tuple(q_fp8.shape) == (T, H, ROW) and q_fp8.is_contiguous(),
+          "q_fp8 must be a contiguous 1-byte [T, H, 128] tensor")
+    for name, t in (("weights_out", weights_out), ("q_scale_out", q_scale_out)):
+        if t is not None:
+            _need(t.dtype == torch.float32 and tuple(t.shape) == (T, H) and t.is_contiguous(),
+                  "%s must be contiguous float32 [T, H]" % name)
+    return DsaidxQArgs(_ptr(q), q.stride(0), q.stride(1), _ptr(weights), weights.stride(0),
+                       _ptr(positions), T, H, float(weight_scale), _ptr(q_fp8),
+                       _ptr(weights_out), _ptr(q_scale_out))
+
+
+def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cache,
+           k_scale) -> DsaidxKArgs:
+    """k: bf16 [T, 128] (unit inner stride); ln_gamma/ln_beta float32 [128];
+    positions/out_cache_loc int64 [T]; k_cache 1-byte [S, >=128] (unit inner
+    stride; codes go to the first 128 bytes of each row); k_scale float32 [S]."""
+    import torch
+    _need(k.dtype == torch.bfloat16 and k.dim() == 2 and k.shape[1] == ROW and k.stride(1) == 1,
+          "k must be bf16 [T, 128] with unit inner stride")
+    T = k.shape[0]
+    for name, t in (("ln_gamma", ln_gamma), ("ln_beta", ln_beta)):
+        _need(t.dtype == torch.float32 and t.numel() == ROW and t.is_contiguous(),
+              "%s must be contiguous float32 [128]" % name)
+    for name, t in (("positions", positions), ("out_cache_loc", out_cache_loc)):
+        _need(t.dtype == torch.int64 and t.numel() == T and t.is_contiguous(),
+              "%s must be contiguous int64 [T]" % name)
+    _need(k_cache.element_size() == 1 and k_cache.dim() == 2 and k_cache.shape[1] >= ROW
+          and k_cache.stride(1) == 1, "k_cache must be a 1-byte [S, >=128] tensor")
+    S = k_cache.shape[0]
+    _need(k_scale.dtype == torch.float32 and k_scale.numel() == S and k_scale.is_contiguous(),
+          "k_scale must be contiguous float32 [S]")
+    return DsaidxKArgs(_ptr(k), k.stride(0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps), 0,
+                       _ptr(positions), _ptr(out_cache_loc), T, _ptr(k_cache), k_cache.stride(0),
+                       _ptr(k_scale), S)

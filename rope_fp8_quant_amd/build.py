@@ -1,0 +1,69 @@
+"""Build libdsaidx.so in-tree with hipcc for gfx950.
+
+    python -m rope_fp8_quant_amd.build
+
+Device code is compiled without floating-point contraction (the arithmetic is
+defined op by op) and without packed-fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG, "libdsaidx.so")
+ARCH = "gfx950"
+
+SOURCES = ["dsaidx_kernels.hip", "dsaidx_api.cpp"]
+HEADERS = [os.path.join(INCLUDE, "dsaidx.h"), os.path.join(CSRC, "dsaidx_internal.h")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libdsaidx)")
+
+
+def common_flags():
+    return ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+            "-ffp-contract=off", "-I" + INCLUDE, "-I" + CSRC]
+
+
+def device_flags():
+    return ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False, extra_defines=()) -> str:
+    """Compile every source and link libdsaidx.so; returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmd = [cc] + common_flags() + ["-D" + d for d in extra_defines]
+        if src.endswith(".hip"):
+            cmd += device_flags() + ["-x", "hip"]
+        cmd += ["-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [cc, "-shared", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,271 @@
+// C-ABI host layer of libdsaidx: argument checks, launch shape, status codes.
+// The operation and the argument contract are documented in include/dsaidx.h.
+#include "dsaidx.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "dsaidx_internal.h"
+
+namespace {
+
+using dsaidx::PrepParams;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 40;
+constexpr int32_t kMaxHeads = 4096;
+constexpr unsigned kBlock = 256;          // 4 wavefronts
+constexpr unsigned kSmallBlock = 64;      // 1 wavefront (k-only launch shape)
+constexpr int kQueryBlocksPerCU = 8;      // grid-stride cap for query work
+constexpr int kKeyBlockDivisor = 16;      // key blocks = query blocks / 16 in one dispatch
+
+bool token_count_ok(int64_t t) { return t >= 0 && t <= kMaxTokens; }
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+dsaidx_status check_rope(const dsaidx_rope* r) {
+    if (!r->cos || !r->sin) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!aligned(r->cos, 16) || !aligned(r->sin, 16)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (r->rope_dim < 16 || r->rope_dim > dsaidx::kRow || r->rope_dim % 16 != 0)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (r->style != DSAIDX_ROPE_NEOX && r->style != DSAIDX_ROPE_INTERLEAVED)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (r->row_stride < r->rope_dim / 2 || r->row_stride % 4 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (r->max_position < 1) return DSAIDX_ERR_INVALID_ARGUMENT;
+    return DSAIDX_OK;
+}
+
+dsaidx_status check_q(const dsaidx_q_args* q) {
+    if (q->num_heads < 1 || q->num_heads > kMaxHeads) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(q->weight_scale)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!q->q || !q->weights || !q->positions || !q->q_fp8 || !q->weights_out)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!aligned(q->q, 16) || !aligned(q->weights, 2) || !aligned(q->positions, 8) ||
+        !aligned(q->q_fp8, 8) || !aligned(q->weights_out, 4) ||
+        (q->q_scale_out && !aligned(q->q_scale_out, 4)))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (q->q_stride_h < dsaidx::kRow || q->q_stride_h % 8 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (q->q_stride_t % 8 != 0 ||
+        q->q_stride_t < (int64_t)(q->num_heads - 1) * q->q_stride_h + dsaidx::kRow)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (q->w_stride_t < q->num_heads) return DSAIDX_ERR_INVALID_ARGUMENT;
+    return DSAIDX_OK;
+}
+
+dsaidx_status check_k(const dsaidx_k_args* k) {
+    if (!k->k || !k->ln_gamma || !k->ln_beta || !k->positions || !k->out_cache_loc ||
+        !k->k_cache || !k->k_scale)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!aligned(k->k, 16) || !aligned(k->ln_gamma, 16) || !aligned(k->ln_beta, 16) ||
+        !aligned(k->positions, 8) || !aligned(k->out_cache_loc, 8) || !aligned(k->k_cache, 8) ||
+        !aligned(k->k_scale, 4))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->k_stride_t < dsaidx::kRow || k->k_stride_t % 8 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!(k->ln_eps > 0.0f) || !std::isfinite(k->ln_eps)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->flags != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->k_cache_row_stride < dsaidx::kRow || k->k_cache_row_stride % 8 != 0)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->num_slots < 1) return DSAIDX_ERR_INVALID_ARGUMENT;
+    return DSAIDX_OK;
+}
+
+void fill_rope(PrepParams& p, const dsaidx_rope& r) {
+    p.cos = r.cos;
+    p.sin = r.sin;
+    p.rs = r.row_stride;
+    p.P = r.max_position;
+    p.R = r.rope_dim;
+}
+
+void fill_q(PrepParams& p, const dsaidx_q_args& q) {
+    p.q = q.q;
+    p.q_st = q.q_stride_t;
+    p.q_sh = q.q_stride_h;
+    p.w = q.weights;
+    p.w_st = q.w_stride_t;
+    p.q_pos = q.positions;
+    p.q_fp8 = q.q_fp8;
+    p.w_out = q.weights_out;
+    p.q_scale = q.q_scale_out;
+    p.weight_scale = q.weight_scale;
+    p.H = q.num_heads;
+    p.head_blocks = (q.num_heads + dsaidx::kHeadsPerItem - 1) / dsaidx::kHeadsPerItem;
+    p.q_items = q.num_tokens * p.head_blocks;
+    p.T = q.num_tokens;
+}
+
+void fill_k(PrepParams& p, const dsaidx_k_args& k) {
+    p.k = k.k;
+    p.k_st = k.k_stride_t;
+    p.gamma = k.ln_gamma;
+    p.beta = k.ln_beta;
+    p.eps = k.ln_eps;
+    p.k_pos = k.positions;
+    p.loc = k.out_cache_loc;
+    p.k_cache = k.k_cache;
+    p.k_row_stride = k.k_cache_row_stride;
+    p.k_scale = k.k_scale;
+    p.S = k.num_slots;
+    p.k_items = (k.num_tokens + dsaidx::kTokensPerKItem - 1) / dsaidx::kTokensPerKItem;
+    p.T = k.num_tokens;
+}
+
+// Compute units of the current device, cached per device index.
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+dsaidx_status to_status(hipError_t err) {
+    if (err == hipSuccess) return DSAIDX_OK;
+    if (err == hipErrorNoDevice || err == hipErrorInvalidDeviceFunction ||
+        err == hipErrorNoBinaryForGpu || err == hipErrorInsufficientDriver)
+        return DSAIDX_ERR_UNSUPPORTED;
+    return DSAIDX_ERR_HIP;
+}
+
+dsaidx_status launch(const PrepParams& p, int style, int64_t grid, unsigned block,
+                     dsaidx_stream_t stream) {
+    if (grid <= 0) return DSAIDX_OK;
+    return to_status(dsaidx::launch_prep(p, style, (unsigned)grid, block,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+int64_t query_blocks(int64_t q_items) {
+    const int64_t cap = (int64_t)compute_units() * kQueryBlocksPerCU;
+    const int64_t need = ceil_div(q_items, kBlock / 64);
+    return need < cap ? need : cap;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsaidx_status dsaidx_q_rope_quant_fold(const dsaidx_q_args* q, const dsaidx_rope* rope,
+                                       dsaidx_stream_t stream) {
+    if (!q || !rope || !token_count_ok(q->num_tokens)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (q->num_tokens == 0) return DSAIDX_OK;
+    dsaidx_status st = check_rope(rope);
+    if (st == DSAIDX_OK) st = check_q(q);
+    if (st != DSAIDX_OK) return st;
+    PrepParams p;
+    std::memset(&p, 0, sizeof p);
+    fill_rope(p, *rope);
+    fill_q(p, *q);
+    p.k_blocks = 0;
+    return launch(p, rope->style, query_blocks(p.q_items), kBlock, stream);
+}
+
+dsaidx_status dsaidx_k_norm_rope_quant_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
+                                             dsaidx_stream_t stream) {
+    if (!k || !rope || !token_count_ok(k->num_tokens)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->num_tokens == 0) return DSAIDX_OK;
+    dsaidx_status st = check_rope(rope);
+    if (st == DSAIDX_OK) st = check_k(k);
+    if (st != DSAIDX_OK) return st;
+    PrepParams p;
+    std::memset(&p, 0, sizeof p);
+    fill_rope(p, *rope);
+    fill_k(p, *k);
+    const int64_t cap = (int64_t)compute_units() * kQueryBlocksPerCU;
+    int64_t kb = ceil_div(p.k_items, kBlock / 64);
+    if (kb > cap) kb = cap;
+    p.k_blocks = (int32_t)kb;
+    return launch(p, rope->style, kb, kBlock, stream);
+}
+
+dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
+                                          dsaidx_stream_t stream) {
+    if (!k || !rope || !token_count_ok(k->num_tokens)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->num_tokens == 0) return DSAIDX_OK;
+    dsaidx_status st = check_rope(rope);
+    if (st == DSAIDX_OK) st = check_k(k);
+    if (st != DSAIDX_OK) return st;
+    PrepParams p;
+    std::memset(&p, 0, sizeof p);
+    fill_rope(p, *rope);
+    fill_k(p, *k);
+    // One wavefront per workgroup, one work item per wavefront while that
+    // fills the chip: few tokens spread over as many CUs as possible.
+    const int64_t cap = (int64_t)compute_units() * kQueryBlocksPerCU * 4;
+    int64_t kb = p.k_items < cap ? p.k_items : cap;
+    p.k_blocks = (int32_t)kb;
+    return launch(p, rope->style, kb, kSmallBlock, stream);
+}
+
+dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
+                              const dsaidx_rope* rope, dsaidx_stream_t stream) {
+    if (!q || !k || !rope || !token_count_ok(q->num_tokens) || q->num_tokens != k->num_tokens)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (q->num_tokens == 0) return DSAIDX_OK;
+    dsaidx_status st = check_rope(rope);
+    if (st == DSAIDX_OK) st = check_q(q);
+    if (st == DSAIDX_OK) st = check_k(k);
+    if (st != DSAIDX_OK) return st;
+    PrepParams p;
+    std::memset(&p, 0, sizeof p);
+    fill_rope(p, *rope);
+    fill_q(p, *q);
+    fill_k(p, *k);
+    const int64_t qb = query_blocks(p.q_items);
+    int64_t kb = ceil_div(p.k_items, kBlock / 64);
+    const int64_t kcap = ceil_div(qb, kKeyBlockDivisor);
+    if (kb > kcap) kb = kcap;
+    p.k_blocks = (int32_t)kb;
+    return launch(p, rope->style, qb + kb, kBlock, stream);
+}
+
+dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,
+                                         dsaidx_stream_t stream) {
+    if (n < 0 || !in || !out || !aligned(in, 4) || !aligned(out, 8))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (n == 0) return DSAIDX_OK;
+    const int64_t cap = (int64_t)compute_units() * 32;
+    int64_t grid = ceil_div(ceil_div(n, 8), 256);
+    if (grid > cap) grid = cap;
+    return to_status(dsaidx::launch_fp8_selftest(in, out, n, (unsigned)grid,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int dsaidx_device_supported(int device) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count) return 0;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+const char* dsaidx_status_string(dsaidx_status status) {
+    switch (status) {
+        case DSAIDX_OK: return "DSAIDX_OK";
+        case DSAIDX_ERR_INVALID_ARGUMENT: return "DSAIDX_ERR_INVALID_ARGUMENT";
+        case DSAIDX_ERR_UNSUPPORTED: return "DSAIDX_ERR_UNSUPPORTED";
+        case DSAIDX_ERR_HIP: return "DSAIDX_ERR_HIP";
+    }
+    return "DSAIDX_UNKNOWN_STATUS";
+}
+
+int dsaidx_abi_version(void) { return DSAIDX_ABI_VERSION; }
+
+size_t dsaidx_struct_size(int which) {
+    switch (which) {
+        case 0: return sizeof(dsaidx_rope);
+        case 1: return sizeof(dsaidx_q_args);
+        case 2: return sizeof(dsaidx_k_args);
+    }
+    return 0;
+}
+
+}  // extern "C"

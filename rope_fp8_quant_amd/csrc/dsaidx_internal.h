@@ -1,0 +1,63 @@
+// Private interface between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+constexpr int kRow = 128;           // elements per head vector / key row
+constexpr int kLanesPerRow = 16;    // one DPP row of a wavefront per vector
+constexpr int kRowsPerWave = 4;     // 64 lanes / 16
+constexpr int kHeadsPerItem = 16;   // query heads per wavefront work item
+constexpr int kTokensPerKItem = 4;  // key rows per wavefront work item
+
+// Everything one dispatch needs.  Blocks [0, k_blocks) run key work items,
+// blocks [k_blocks, gridDim.x) run query work items; either range may be empty.
+struct PrepParams {
+    // query rows: item = (token, block of 16 heads)
+    const uint16_t* q;
+    int64_t q_st, q_sh;
+    const uint16_t* w;
+    int64_t w_st;
+    const int64_t* q_pos;
+    uint8_t* q_fp8;
+    float* w_out;
+    float* q_scale;
+    float weight_scale;
+    int32_t H;
+    int32_t head_blocks;  // ceil(H / 16)
+    int32_t k_blocks;
+    int64_t q_items;      // T * head_blocks (0 when the dispatch has no query work)
+    // key rows: item = 4 consecutive tokens
+    const uint16_t* k;
+    int64_t k_st;
+    const float* gamma;
+    const float* beta;
+    const int64_t* k_pos;
+    const int64_t* loc;
+    uint8_t* k_cache;
+    int64_t k_row_stride;  // bytes
+    float* k_scale;
+    int64_t S;
+    int64_t k_items;       // ceil(T / 4) (0 when the dispatch has no key work)
+    int64_t T;
+    float eps;
+    // rope table
+    int32_t R;
+    const float* cos;
+    const float* sin;
+    int64_t rs;            // floats between table rows
+    int64_t P;             // table rows
+};
+
+// Enqueue one dispatch of the preparation kernel for rope style 0 (NeoX) or 1
+// (interleaved).
+hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned block,
+                       hipStream_t stream);
+
+// Enqueue the stand-alone E4M3FN conversion (self-test of the device encoder).
+hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigned grid,
+                               hipStream_t stream);
+
+}  // namespace dsaidx

@@ -1,0 +1,191 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/dsaidx.h declares, agree
+with the binding on struct layout, and reject bad arguments on the host before
+any HIP call (so these run on a machine without a GPU).  Device pointers here
+are fake, aligned addresses: the library never dereferences them on the host.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rope_fp8_quant_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+FAKE = 0x10000  # aligned, never dereferenced on the host
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(HEADER_DIR):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(dsaidx_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from rope_fp8_quant_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(B.EXPORTED) == set(names)
+
+
+def test_abi_version_and_struct_sizes(L):
+    assert B.dsaidx_abi_version() == 1
+    assert L.dsaidx_struct_size(0) == ctypes.sizeof(B.DsaidxRope) == 40
+    assert L.dsaidx_struct_size(1) == ctypes.sizeof(B.DsaidxQArgs) == 88
+    assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 96
+    assert L.dsaidx_struct_size(7) == 0
+
+
+def test_status_strings(L):
+    assert B.status_string(0) == "DSAIDX_OK"
+    assert B.status_string(1) == "DSAIDX_ERR_INVALID_ARGUMENT"
+    assert B.status_string(2) == "DSAIDX_ERR_UNSUPPORTED"
+    assert B.status_string(3) == "DSAIDX_ERR_HIP"
+    assert B.status_string(99) == "DSAIDX_UNKNOWN_STATUS"
+
+
+def test_device_supported_without_gpu_does_not_crash(L):
+    v = L.dsaidx_device_supported(0)
+    assert v in (0, 1)
+    assert L.dsaidx_device_supported(-1) == 0
+    assert L.dsaidx_device_supported(1 << 20) == 0
+
+
+def good_rope(**kw):
+    r = B.DsaidxRope(FAKE, FAKE + 128, 64, 4096, 64, 0)
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return r
+
+
+def good_q(T=1, **kw):
+    q = B.DsaidxQArgs(FAKE, 64 * 128, 128, FAKE, 64, FAKE, T, 64, 1.0, FAKE, FAKE, None)
+    for k, v in kw.items():
+        setattr(q, k, v)
+    return q
+
+
+def good_k(T=1, **kw):
+    k = B.DsaidxKArgs(FAKE, 128, FAKE, FAKE, 1e-6, 0, FAKE, FAKE, T, FAKE, 128, FAKE, 4096)
+    for k_, v in kw.items():
+        setattr(k, k_, v)
+    return k
+
+
+def call_q(L, q, r):
+    return L.dsaidx_q_rope_quant_fold(ctypes.byref(q), ctypes.byref(r), None)
+
+
+def call_k(L, k, r, entry="dsaidx_k_norm_rope_quant_store"):
+    return getattr(L, entry)(ctypes.byref(k), ctypes.byref(r), None)
+
+
+def call_fused(L, q, k, r):
+    return L.dsaidx_qk_fused(ctypes.byref(q), ctypes.byref(k), ctypes.byref(r), None)
+
+
+def test_empty_calls_are_ok_without_launch(L):
+    r = good_rope()
+    assert call_q(L, good_q(T=0), r) == B.DSAIDX_OK
+    assert call_k(L, good_k(T=0), r) == B.DSAIDX_OK
+    assert call_k(L, good_k(T=0), r, "dsaidx_k_only_prepare_store") == B.DSAIDX_OK
+    assert call_fused(L, good_q(T=0), good_k(T=0), r) == B.DSAIDX_OK
+    # empty tensors may carry NULL data pointers
+    null_q = B.DsaidxQArgs()
+    null_k = B.DsaidxKArgs()
+    null_r = B.DsaidxRope()
+    assert call_q(L, null_q, null_r) == B.DSAIDX_OK
+    assert call_k(L, null_k, null_r) == B.DSAIDX_OK
+    assert call_fused(L, null_q, null_k, null_r) == B.DSAIDX_OK
+
+
+def test_null_structs_rejected(L):
+    assert L.dsaidx_q_rope_quant_fold(None, ctypes.byref(good_rope()), None) == 1
+    assert L.dsaidx_qk_fused(ctypes.byref(good_q()), ctypes.byref(good_k()), None, None) == 1
+    assert L.dsaidx_q_rope_quant_fold(ctypes.byref(good_q()), None, None) == 1
+    assert L.dsaidx_k_norm_rope_quant_store(None, ctypes.byref(good_rope()), None) == 1
+    assert L.dsaidx_k_only_prepare_store(None, ctypes.byref(good_rope()), None) == 1
+    assert L.dsaidx_qk_fused(ctypes.byref(good_q()), None, ctypes.byref(good_rope()), None) == 1
+
+
+BAD_ROPE = [dict(cos=None), dict(sin=None), dict(cos=FAKE + 4), dict(rope_dim=0),
+            dict(rope_dim=8), dict(rope_dim=48 + 8), dict(rope_dim=144), dict(style=2),
+            dict(style=-1), dict(row_stride=16), dict(row_stride=34), dict(max_position=0)]
+
+
+@pytest.mark.parametrize("kw", BAD_ROPE, ids=lambda d: str(d))
+def test_bad_rope_rejected(L, kw):
+    r = good_rope(**kw)
+    assert call_q(L, good_q(), r) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_k(L, good_k(), r) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+BAD_Q = [dict(q=None), dict(weights=None), dict(positions=None), dict(q_fp8=None),
+         dict(weights_out=None), dict(q=FAKE + 8), dict(positions=FAKE + 4),
+         dict(q_fp8=FAKE + 4), dict(weights_out=FAKE + 2), dict(q_scale_out=FAKE + 2),
+         dict(weights=FAKE + 1), dict(num_tokens=-1), dict(num_heads=0), dict(num_heads=5000),
+         dict(q_stride_h=120), dict(q_stride_h=132), dict(q_stride_t=63 * 128),
+         dict(q_stride_t=64 * 128 + 4), dict(w_stride_t=63), dict(weight_scale=float("inf")),
+         dict(weight_scale=float("nan"))]
+
+
+@pytest.mark.parametrize("kw", BAD_Q, ids=lambda d: str(d))
+def test_bad_q_rejected(L, kw):
+    q = good_q(**kw)
+    assert call_q(L, q, good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_fused(L, q, good_k(), good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+BAD_K = [dict(k=None), dict(ln_gamma=None), dict(ln_beta=None), dict(positions=None),
+         dict(out_cache_loc=None), dict(k_cache=None), dict(k_scale=None),
+         dict(k=FAKE + 8), dict(ln_gamma=FAKE + 4), dict(out_cache_loc=FAKE + 4),
+         dict(k_cache=FAKE + 4), dict(k_scale=FAKE + 2), dict(num_tokens=-3),
+         dict(k_stride_t=64), dict(k_stride_t=130), dict(ln_eps=0.0), dict(ln_eps=-1e-6),
+         dict(ln_eps=float("nan")), dict(ln_eps=float("inf")), dict(flags=1),
+         dict(k_cache_row_stride=120), dict(k_cache_row_stride=132), dict(num_slots=0)]
+
+
+@pytest.mark.parametrize("kw", BAD_K, ids=lambda d: str(d))
+def test_bad_k_rejected(L, kw):
+    k = good_k(**kw)
+    for entry in ("dsaidx_k_norm_rope_quant_store", "dsaidx_k_only_prepare_store"):
+        assert call_k(L, k, good_rope(), entry) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_fused(L, good_q(), k, good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+def test_fused_token_count_mismatch_rejected(L):
+    assert call_fused(L, good_q(T=3), good_k(T=4), good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_fused(L, good_q(T=0), good_k(T=4), good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_fused(L, good_q(T=2), good_k(T=0), good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("T", [-1, (1 << 40) + 1])
+def test_token_count_range(L, T):
+    assert call_q(L, good_q(T=T), good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_k(L, good_k(T=T), good_rope()) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+def test_fp8_selftest_argument_checks(L):
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, 0, None) == B.DSAIDX_OK
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, -1, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(None, FAKE, 8, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, None, 8, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE + 2, FAKE, 8, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE + 4, 8, None) == 1

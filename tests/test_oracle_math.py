@@ -15,9 +15,9 @@ import numpy as np
 import pytest
 import torch
 
+from golden_util import load_hand_examples
 from rope_fp8_quant_amd import workloads as W
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 ROW = 128
 
 
@@ -71,22 +71,7 @@ def test_scale_closed_form_mantissa_rule(oracle_lib):
 
 # ---------------------------------------------------------- hand fixture ----
 
-def _load_examples():
-    rows = []
-    with open(os.path.join(GOLDEN, "rope_quant_hand_examples.txt")) as f:
-        for line in f:
-            if not line.strip() or line.startswith("#"):
-                continue
-            head, xs, e, codes, folded = [p.strip() for p in line.split("|")]
-            name, style, pos, w = head.split()
-            xs = {int(k): float(v) for k, v in (t.split(":") for t in xs.split())}
-            codes = {int(k): int(v, 16) for k, v in (t.split(":") for t in codes.split())}
-            rows.append((name, 0 if style == "neox" else 1, int(pos), float(w), xs, int(e),
-                         codes, float(folded)))
-    return rows
-
-
-@pytest.mark.parametrize("ex", _load_examples(), ids=lambda r: r[0])
+@pytest.mark.parametrize("ex", load_hand_examples(), ids=lambda r: r[0])
 def test_hand_examples(oracle_lib, ex):
     name, style, pos, w, xs, e, codes, folded = ex
     cos, sin = W.rope_table(8, 64)
