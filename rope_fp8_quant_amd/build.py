@@ -40,14 +40,16 @@ def device_flags():
     return ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, extra_defines=()) -> str:
-    """Compile every source and link libdsaidx.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_defines=(), out_path: str = LIB_PATH,
+          build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link libdsaidx.so; returns the library path.
+    extra_defines / out_path / build_dir serve tuning builds of variants."""
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
     objs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         cmd = [cc] + common_flags() + ["-D" + d for d in extra_defines]
         if src.endswith(".hip"):
             cmd += device_flags() + ["-x", "hip"]
@@ -56,13 +58,13 @@ def build(verbose: bool = False, extra_defines=()) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    tmp = out_path + ".tmp%d" % os.getpid()
     cmd = [cc, "-shared", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

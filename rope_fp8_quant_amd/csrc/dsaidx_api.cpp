@@ -2,7 +2,6 @@
 // The operation and the argument contract are documented in include/dsaidx.h.
 #include "dsaidx.h"
 
-#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -16,8 +15,14 @@ constexpr int64_t kMaxTokens = int64_t(1) << 40;
 constexpr int32_t kMaxHeads = 4096;
 constexpr unsigned kBlock = 256;          // 4 wavefronts
 constexpr unsigned kSmallBlock = 64;      // 1 wavefront (k-only launch shape)
-constexpr int kQueryBlocksPerCU = 8;      // grid-stride cap for query work
-constexpr int kKeyBlockDivisor = 16;      // key blocks = query blocks / 16 in one dispatch
+// Launch shape: one workgroup per 4 work items up to this many workgroups
+// (beyond it the kernels loop).  A one-shot grid streams measurably faster on
+// MI355X than a grid capped near the CU count with long grid-stride loops.
+#ifndef DSAIDX_MAX_GRID
+#define DSAIDX_MAX_GRID (1 << 24)
+#endif
+constexpr int64_t kMaxGrid = DSAIDX_MAX_GRID;
+constexpr int kKeyBlockDivisor = 16;      // fused: key workgroups <= query workgroups / 16
 
 bool token_count_ok(int64_t t) { return t >= 0 && t <= kMaxTokens; }
 
@@ -110,22 +115,6 @@ void fill_k(PrepParams& p, const dsaidx_k_args& k) {
     p.T = k.num_tokens;
 }
 
-// Compute units of the current device, cached per device index.
-int compute_units() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev < 0 || dev >= 64) return 256;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
-
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 dsaidx_status to_status(hipError_t err) {
@@ -143,10 +132,9 @@ dsaidx_status launch(const PrepParams& p, int style, int64_t grid, unsigned bloc
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
-int64_t query_blocks(int64_t q_items) {
-    const int64_t cap = (int64_t)compute_units() * kQueryBlocksPerCU;
-    const int64_t need = ceil_div(q_items, kBlock / 64);
-    return need < cap ? need : cap;
+int64_t capped_grid(int64_t items, unsigned block) {
+    const int64_t need = ceil_div(items, block / 64);
+    return need < kMaxGrid ? need : kMaxGrid;
 }
 
 }  // namespace
@@ -165,7 +153,7 @@ dsaidx_status dsaidx_q_rope_quant_fold(const dsaidx_q_args* q, const dsaidx_rope
     fill_rope(p, *rope);
     fill_q(p, *q);
     p.k_blocks = 0;
-    return launch(p, rope->style, query_blocks(p.q_items), kBlock, stream);
+    return launch(p, rope->style, capped_grid(p.q_items, kBlock), kBlock, stream);
 }
 
 dsaidx_status dsaidx_k_norm_rope_quant_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
@@ -179,9 +167,7 @@ dsaidx_status dsaidx_k_norm_rope_quant_store(const dsaidx_k_args* k, const dsaid
     std::memset(&p, 0, sizeof p);
     fill_rope(p, *rope);
     fill_k(p, *k);
-    const int64_t cap = (int64_t)compute_units() * kQueryBlocksPerCU;
-    int64_t kb = ceil_div(p.k_items, kBlock / 64);
-    if (kb > cap) kb = cap;
+    const int64_t kb = capped_grid(p.k_items, kBlock);
     p.k_blocks = (int32_t)kb;
     return launch(p, rope->style, kb, kBlock, stream);
 }
@@ -197,10 +183,9 @@ dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_r
     std::memset(&p, 0, sizeof p);
     fill_rope(p, *rope);
     fill_k(p, *k);
-    // One wavefront per workgroup, one work item per wavefront while that
-    // fills the chip: few tokens spread over as many CUs as possible.
-    const int64_t cap = (int64_t)compute_units() * kQueryBlocksPerCU * 4;
-    int64_t kb = p.k_items < cap ? p.k_items : cap;
+    // One wavefront per workgroup: few tokens spread over as many CUs as
+    // possible (the dense decode path runs a handful of tokens).
+    const int64_t kb = capped_grid(p.k_items, kSmallBlock);
     p.k_blocks = (int32_t)kb;
     return launch(p, rope->style, kb, kSmallBlock, stream);
 }
@@ -219,7 +204,7 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     fill_rope(p, *rope);
     fill_q(p, *q);
     fill_k(p, *k);
-    const int64_t qb = query_blocks(p.q_items);
+    const int64_t qb = capped_grid(p.q_items, kBlock);
     int64_t kb = ceil_div(p.k_items, kBlock / 64);
     const int64_t kcap = ceil_div(qb, kKeyBlockDivisor);
     if (kb > kcap) kb = kcap;
@@ -232,9 +217,8 @@ dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t 
     if (n < 0 || !in || !out || !aligned(in, 4) || !aligned(out, 8))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (n == 0) return DSAIDX_OK;
-    const int64_t cap = (int64_t)compute_units() * 32;
     int64_t grid = ceil_div(ceil_div(n, 8), 256);
-    if (grid > cap) grid = cap;
+    if (grid > kMaxGrid) grid = kMaxGrid;
     return to_status(dsaidx::launch_fp8_selftest(in, out, n, (unsigned)grid,
                                                  reinterpret_cast<hipStream_t>(stream)));
 }

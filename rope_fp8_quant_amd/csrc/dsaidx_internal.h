@@ -9,11 +9,15 @@ namespace dsaidx {
 constexpr int kRow = 128;           // elements per head vector / key row
 constexpr int kLanesPerRow = 16;    // one DPP row of a wavefront per vector
 constexpr int kRowsPerWave = 4;     // 64 lanes / 16
-constexpr int kHeadsPerItem = 16;   // query heads per wavefront work item
+#ifndef DSAIDX_HEADS_PER_ITEM
+#define DSAIDX_HEADS_PER_ITEM 16
+#endif
+constexpr int kHeadsPerItem = DSAIDX_HEADS_PER_ITEM;  // query heads per wavefront work item
 constexpr int kTokensPerKItem = 4;  // key rows per wavefront work item
 
-// Everything one dispatch needs.  Blocks [0, k_blocks) run key work items,
-// blocks [k_blocks, gridDim.x) run query work items; either range may be empty.
+// Everything one dispatch needs.  k_blocks workgroups run key work items and
+// the others query work items (which ones: see the kernel); either set may be
+// empty.
 struct PrepParams {
     // query rows: item = (token, block of 16 heads)
     const uint16_t* q;

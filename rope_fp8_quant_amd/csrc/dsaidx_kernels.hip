@@ -10,33 +10,137 @@
 //     stored at cache slot out_cache_loc[t].
 //
 // Mapping.  Each 128-wide vector is owned by one 16-lane DPP row of a
-// wavefront: lane j holds elements [8j, 8j+8) from a single 16-byte load, so a
-// wavefront instruction moves four whole 256-byte vectors.  Row reductions
-// (max |y|, LayerNorm sums) are four DPP row_ror steps; the NeoX partner of
-// lane j (elements i and i + rope_dim/2 live rope_dim/16 lanes apart) comes
-// from ds_bpermute.  A query work item is one token and 16 heads (4 passes of
-// 4 vectors): the token's cos/sin sit in registers for all 16 heads.  A key
-// work item is 4 tokens.  One dispatch runs key items on its first k_blocks
-// workgroups and query items on the rest, with grid-stride loops.
+// wavefront, eight elements per lane, so one wavefront instruction covers four
+// whole vectors.  Two lane layouts:
+//   split  lane j holds elements [4j, 4j+4) and [64+4j, 64+4j+4).  Every lane
+//          then owns rope elements when rope_dim = 64, so the rotation costs
+//          half as many instructions per lane; a NeoX pair (i, i + R/2) sits in
+//          lanes j and j + R/8.  Used for NeoX with rope_dim <= 64 and for the
+//          interleaved style (pairs never leave a lane).
+//   contig lane j holds [8j, 8j+8); used for NeoX with rope_dim 80..128.
+// Row reductions (max |y|, LayerNorm sums) are four DPP row_ror steps; the
+// NeoX partner values come from ds_bpermute.  A query work item is one token
+// and 16 heads (4 passes of 4 vectors): the token's cos/sin sit in registers
+// for all 16 heads, and the 16 folded head gates of the item are produced by
+// one coalesced load and store.  A key work item is 4 tokens.  Key and query
+// work items share one dispatch: the last k_blocks workgroups take key items.
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
-// is rounded on its own (contraction is off), the LayerNorm sums are fp64,
-// and the fp8 codes come from the hardware packed convert (round to nearest
-// even; no value can exceed 448 because the scale is chosen from the row max).
+// is rounded on its own (contraction is off), the LayerNorm sums are fp64, and
+// the codes come from the gfx950 scaled packed convert, which rounds x / 2^e
+// to nearest-even E4M3FN -- the same as multiplying by 2^-e (exact) and
+// converting.  No value can exceed 448, as 2^e is chosen from the row max.
 #include "dsaidx_internal.h"
 
 #pragma clang fp contract(off)
 
+// Cache policy of the streamed rows: every q/k row is read once and every code
+// row written once, so they carry the nontemporal hint and do not displace the
+// cos/sin rows, head gates and LayerNorm parameters, which are reused.
+#ifndef DSAIDX_NT_LOADS
+#define DSAIDX_NT_LOADS 1
+#endif
+#ifndef DSAIDX_NT_STORES
+#define DSAIDX_NT_STORES 1
+#endif
+
+// Placement of the key workgroups of a fused dispatch: 0 first, 1 last,
+// 2 spread evenly among the query workgroups.  Last measures best: the query
+// stream starts at once and the latency-bound LayerNorm work of the key rows
+// overlaps its tail.
+#ifndef DSAIDX_K_PLACEMENT
+#define DSAIDX_K_PLACEMENT 1
+#endif
+
 namespace dsaidx {
 namespace {
 
-constexpr int kPasses = kHeadsPerItem / kRowsPerWave;  // 4
+constexpr int kPasses = kHeadsPerItem / kRowsPerWave;
+constexpr int kContig = 0;
+constexpr int kSplit = 1;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 // DPP controls (row = 16 lanes): row_ror:n reads lane (l - n) mod 16 of the row.
 constexpr int kRowRor1 = 0x121;
 constexpr int kRowRor2 = 0x122;
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
+
+// ------------------------------------------------------------ memory ----
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(p);
+#if DSAIDX_NT_LOADS
+    const u32x4 r = __builtin_nontemporal_load(v);
+#else
+    const u32x4 r = *v;
+#endif
+    return make_uint4(r.x, r.y, r.z, r.w);
+}
+
+__device__ __forceinline__ uint2 load8(const uint16_t* p) {
+    const u32x2* v = reinterpret_cast<const u32x2*>(p);
+#if DSAIDX_NT_LOADS
+    const u32x2 r = __builtin_nontemporal_load(v);
+#else
+    const u32x2 r = *v;
+#endif
+    return make_uint2(r.x, r.y);
+}
+
+__device__ __forceinline__ void store8(uint8_t* p, uint2 c) {
+    u32x2* v = reinterpret_cast<u32x2*>(p);
+    const u32x2 w = {c.x, c.y};
+#if DSAIDX_NT_STORES
+    __builtin_nontemporal_store(w, v);
+#else
+    *v = w;
+#endif
+}
+
+__device__ __forceinline__ void store4(uint8_t* p, uint32_t c) {
+    uint32_t* v = reinterpret_cast<uint32_t*>(p);
+#if DSAIDX_NT_STORES
+    __builtin_nontemporal_store(c, v);
+#else
+    *v = c;
+#endif
+}
+
+// The lane's eight bf16 values of one 128-element row (layout order).
+template <int LAYOUT>
+__device__ __forceinline__ uint4 load_row(const uint16_t* row, int j) {
+    if (LAYOUT == kContig) return load16(row + 8 * j);
+    const uint2 a = load8(row + 4 * j);
+    const uint2 b = load8(row + 64 + 4 * j);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// The lane's eight codes of one 128-byte code row.
+template <int LAYOUT>
+__device__ __forceinline__ void store_row(uint8_t* row, int j, uint2 c) {
+    if (LAYOUT == kContig) {
+        store8(row + 8 * j, c);
+    } else {
+        store4(row + 4 * j, c.x);
+        store4(row + 64 + 4 * j, c.y);
+    }
+}
+
+// The lane's eight fp32 LayerNorm parameters (layout order).
+template <int LAYOUT>
+__device__ __forceinline__ void load_params(const float* v, int j, float out[8]) {
+    const float4* p = reinterpret_cast<const float4*>(v);
+    const float4 a = LAYOUT == kContig ? p[2 * j] : p[j];
+    const float4 b = LAYOUT == kContig ? p[2 * j + 1] : p[16 + j];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// --------------------------------------------------------- arithmetic ----
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -48,9 +152,11 @@ __device__ __forceinline__ void unpack8(const uint4& r, float x[8]) {
     x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
 }
 
+// row_ror reads a lane of the same row, always valid, so bound_ctrl changes
+// nothing; it lets the move fold into the consuming op (v_max_u32_dpp).
 template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL>
@@ -61,12 +167,14 @@ __device__ __forceinline__ double dpp_f64(double v) {
     return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
 }
 
-// Max over the 16 lanes of a DPP row; every lane gets the result.
-__device__ __forceinline__ float row_max(float v) {
-    v = fmaxf(v, dpp_f32<kRowRor8>(v));
-    v = fmaxf(v, dpp_f32<kRowRor4>(v));
-    v = fmaxf(v, dpp_f32<kRowRor2>(v));
-    v = fmaxf(v, dpp_f32<kRowRor1>(v));
+// Max over the 16 lanes of a DPP row of non-negative fp32 values given as bit
+// patterns (for x, y >= 0 the unsigned order of the bits is the order of the
+// values); every lane gets the result.
+__device__ __forceinline__ uint32_t row_max_bits(uint32_t v) {
+    v = max(v, dpp_u32<kRowRor8>(v));
+    v = max(v, dpp_u32<kRowRor4>(v));
+    v = max(v, dpp_u32<kRowRor2>(v));
+    v = max(v, dpp_u32<kRowRor1>(v));
     return v;
 }
 
@@ -80,10 +188,19 @@ __device__ __forceinline__ double row_sum(double v) {
     return v;
 }
 
+// Lane-local max |y| of eight values, as bits.
+__device__ __forceinline__ uint32_t lane_amax_bits(const float y[8]) {
+    float am = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) am = fmaxf(am, fabsf(y[m]));
+    return __float_as_uint(am);
+}
+
 // Scale exponent: the smallest e with max(amax, 1e-4) <= 448 * 2^e.  For a
-// normal g = 1.f * 2^E, 448 = 1.75 * 2^8 gives e = E - 8 + [f > 0.75].
-__device__ __forceinline__ int scale_exponent(float amax) {
-    const uint32_t b = __float_as_uint(fmaxf(amax, 1e-4f));
+// normal g = 1.f * 2^E, 448 = 1.75 * 2^8 gives e = E - 8 + [f > 0.75].  The
+// floor (zero-row guard) is applied on the bits, which order like the values.
+__device__ __forceinline__ int scale_exponent(uint32_t amax_bits) {
+    const uint32_t b = max(amax_bits, __float_as_uint(1e-4f));
     return (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
 }
 
@@ -91,59 +208,87 @@ __device__ __forceinline__ float exp2_int(int e) {
     return __uint_as_float((uint32_t)(127 + e) << 23);
 }
 
-// Eight fp32 values (already in [-448, 448]) -> eight E4M3FN bytes, element m
-// in byte m.
-__device__ __forceinline__ uint2 encode8(const float v[8]) {
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
-    return make_uint2((uint32_t)lo, (uint32_t)hi);
+// Eight values -> eight E4M3FN bytes of y / scale (scale a power of two that
+// brings every |y| within 448); element m lands in byte m of the pair of words.
+__device__ __forceinline__ uint2 encode8(const float y[8], float scale) {
+    // The first convert of each word writes its low half; the old operand's
+    // bits are all replaced by the second convert, so any register serves.
+    i16x2 lo = __builtin_bit_cast(i16x2, __float_as_uint(y[0]));
+    i16x2 hi = __builtin_bit_cast(i16x2, __float_as_uint(y[4]));
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[0], y[1], scale, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[2], y[3], scale, true);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[4], y[5], scale, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[6], y[7], scale, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
+// ---------------------------------------------------------------- rope ----
+
 // Per-lane RoPE state for one table row.
-//   NeoX: lanes j < R/16 hold first-half elements, lanes R/16 <= j < R/8 the
-//     matching second half; c[m], s[m] are the angles of the lane's element m
-//     with the sign of the sine folded in (a*c - b*s == a*c + b*(-s) exactly).
-//   Interleaved: lanes j < R/8 hold four whole pairs; c[0..3], s[0..3].
+//   contig NeoX: lanes j < R/16 hold first-half elements, R/16 <= j < R/8 the
+//     second half; c[m], s[m] for the lane's element m.
+//   split NeoX (R <= 64): lanes j < R/8 hold first-half elements in their
+//     first four values, R/8 <= j < R/4 the second half; c[0..3], s[0..3].
+//   split interleaved: the first four values hold pairs 2j, 2j+1 (c[0..1],
+//     s[0..1]) when 4j < R, the last four pairs 32+2j, 33+2j (c[2..3],
+//     s[2..3]) when 64 + 4j < R.
+// For NeoX the sine carries the pair's sign: a*c - b*s == a*c + b*(-s) exactly.
 struct RopeLane {
     float c[8];
     float s[8];
     int partner_addr;  // ds_bpermute byte address of the NeoX partner lane
-    bool active;
+    bool active;       // NeoX: the lane rotates; interleaved: first four values rotate
+    bool active_hi;    // interleaved: last four values rotate
 };
 
-template <int STYLE>
+template <int STYLE, int LAYOUT>
 __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, int lane) {
     RopeLane r;
     const int j = lane & (kLanesPerRow - 1);
     const int R = p.R;
-    const int64_t rowoff = pos * p.rs;
+    const float* crow = p.cos + pos * p.rs;
+    const float* srow = p.sin + pos * p.rs;
+    r.active_hi = false;
+    r.partner_addr = lane << 2;
     if (STYLE == 0) {
-        const int hl = R >> 4;  // lanes per half of the rope slice
+        // lanes per half of the rope slice
+        const int hl = LAYOUT == kContig ? (R >> 4) : (R >> 3);
         r.active = j < 2 * hl;
         const bool first = j < hl;
         const int pj = first ? j + hl : j - hl;
         r.partner_addr = ((lane & ~(kLanesPerRow - 1)) | (r.active ? pj : j)) << 2;
         if (r.active) {
-            const int base = 8 * (first ? j : j - hl);
-            const float4* cp = reinterpret_cast<const float4*>(p.cos + rowoff + base);
-            const float4* sp = reinterpret_cast<const float4*>(p.sin + rowoff + base);
-            const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-            r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
-            r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
             const float sg = first ? -1.0f : 1.0f;
-            r.s[0] = sg * s0.x; r.s[1] = sg * s0.y; r.s[2] = sg * s0.z; r.s[3] = sg * s0.w;
-            r.s[4] = sg * s1.x; r.s[5] = sg * s1.y; r.s[6] = sg * s1.z; r.s[7] = sg * s1.w;
+            if (LAYOUT == kContig) {
+                const int base = 8 * (first ? j : j - hl);
+                const float4 c0 = *reinterpret_cast<const float4*>(crow + base);
+                const float4 c1 = *reinterpret_cast<const float4*>(crow + base + 4);
+                const float4 s0 = *reinterpret_cast<const float4*>(srow + base);
+                const float4 s1 = *reinterpret_cast<const float4*>(srow + base + 4);
+                r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
+                r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
+                r.s[0] = sg * s0.x; r.s[1] = sg * s0.y; r.s[2] = sg * s0.z; r.s[3] = sg * s0.w;
+                r.s[4] = sg * s1.x; r.s[5] = sg * s1.y; r.s[6] = sg * s1.z; r.s[7] = sg * s1.w;
+            } else {
+                const int base = 4 * (first ? j : j - hl);
+                const float4 c0 = *reinterpret_cast<const float4*>(crow + base);
+                const float4 s0 = *reinterpret_cast<const float4*>(srow + base);
+                r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
+                r.s[0] = sg * s0.x; r.s[1] = sg * s0.y; r.s[2] = sg * s0.z; r.s[3] = sg * s0.w;
+            }
         }
     } else {
-        r.active = j < (R >> 3);
-        r.partner_addr = lane << 2;
+        r.active = 4 * j < R;
+        r.active_hi = 64 + 4 * j < R;
         if (r.active) {
-            const float4 c0 = *reinterpret_cast<const float4*>(p.cos + rowoff + 4 * j);
-            const float4 s0 = *reinterpret_cast<const float4*>(p.sin + rowoff + 4 * j);
-            r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
-            r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
+            const float2 c0 = *reinterpret_cast<const float2*>(crow + 2 * j);
+            const float2 s0 = *reinterpret_cast<const float2*>(srow + 2 * j);
+            r.c[0] = c0.x; r.c[1] = c0.y; r.s[0] = s0.x; r.s[1] = s0.y;
+        }
+        if (r.active_hi) {
+            const float2 c1 = *reinterpret_cast<const float2*>(crow + 32 + 2 * j);
+            const float2 s1 = *reinterpret_cast<const float2*>(srow + 32 + 2 * j);
+            r.c[2] = c1.x; r.c[3] = c1.y; r.s[2] = s1.x; r.s[3] = s1.y;
         }
     }
     return r;
@@ -153,101 +298,139 @@ __device__ __forceinline__ int64_t clamp_position(int64_t pos, int64_t P) {
     return pos < 0 ? 0 : (pos >= P ? P - 1 : pos);
 }
 
-// NeoX rotation of the lane's eight values, given the partner lane's eight.
+// One rotated pair: (a, b) -> (a*c - b*s, b*c + a*s).
+__device__ __forceinline__ void rotate_pair(float& a, float& b, float c, float s) {
+    const float ac = a * c;
+    const float bs = b * s;
+    const float bc = b * c;
+    const float as = a * s;
+    a = ac - bs;
+    b = bc + as;
+}
+
+// NeoX rotation of the lane's first N values given the partner's N values.
+template <int N>
 __device__ __forceinline__ void rotate_neox(float x[8], const float xp[8], const RopeLane& r) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < N; ++m) {
         const float xc = x[m] * r.c[m];
         const float ps = xp[m] * r.s[m];
         x[m] = xc + ps;
     }
 }
 
-// Interleaved rotation of the lane's four pairs.
-__device__ __forceinline__ void rotate_interleaved(float x[8], const RopeLane& r) {
+// RoPE of one row held as eight fp32 values per lane.
+template <int STYLE, int LAYOUT>
+__device__ __forceinline__ void rope_row(float x[8], const RopeLane& rl) {
+    if (STYLE == 0) {
+        float xp[8];
+        if (LAYOUT == kContig) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const float a = x[2 * m], b = x[2 * m + 1];
-        const float ac = a * r.c[m];
-        const float bs = b * r.s[m];
-        const float bc = b * r.c[m];
-        const float as = a * r.s[m];
-        x[2 * m] = ac - bs;
-        x[2 * m + 1] = bc + as;
+            for (int m = 0; m < 8; ++m)
+                xp[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(rl.partner_addr, __float_as_int(x[m])));
+            if (rl.active) rotate_neox<8>(x, xp, rl);
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                xp[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(rl.partner_addr, __float_as_int(x[m])));
+            if (rl.active) rotate_neox<4>(x, xp, rl);
+        }
+    } else {
+        if (rl.active) {
+            rotate_pair(x[0], x[1], rl.c[0], rl.s[0]);
+            rotate_pair(x[2], x[3], rl.c[1], rl.s[1]);
+        }
+        if (rl.active_hi) {
+            rotate_pair(x[4], x[5], rl.c[2], rl.s[2]);
+            rotate_pair(x[6], x[7], rl.c[3], rl.s[3]);
+        }
     }
 }
 
-// Row max -> exponent -> codes for the lane's eight values.
-__device__ __forceinline__ uint2 quantize8(const float y[8], int& e_out) {
-    float am = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) am = fmaxf(am, fabsf(y[m]));
-    am = row_max(am);
-    const int e = scale_exponent(am);
-    const float inv = exp2_int(-e);
-    float v[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) v[m] = y[m] * inv;
-    e_out = e;
-    return encode8(v);
+// Same, for a query row still packed as bf16: the NeoX exchange moves the
+// packed words (half as many permutes as fp32 values).
+template <int STYLE, int LAYOUT>
+__device__ __forceinline__ void rope_packed_row(const uint4& raw, float x[8], const RopeLane& rl) {
+    unpack8(raw, x);
+    if (STYLE == 0) {
+        uint4 pr = raw;
+        pr.x = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw.x);
+        pr.y = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw.y);
+        if (LAYOUT == kContig) {
+            pr.z = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw.z);
+            pr.w = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw.w);
+        }
+        float xp[8];
+        unpack8(pr, xp);
+        if (rl.active) {
+            if (LAYOUT == kContig)
+                rotate_neox<8>(x, xp, rl);
+            else
+                rotate_neox<4>(x, xp, rl);
+        }
+    } else {
+        rope_row<STYLE, LAYOUT>(x, rl);
+    }
 }
 
-template <int STYLE>
+// ---------------------------------------------------------- work items ----
+
+template <int STYLE, int LAYOUT>
 __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, int lane) {
     const int g = lane >> 4;
     const int j = lane & (kLanesPerRow - 1);
     const int64_t t = item / p.head_blocks;
     const int hb = (int)(item - t * p.head_blocks);
     const int64_t pos = clamp_position(p.q_pos[t], p.P);
-    const RopeLane rl = rope_lane<STYLE>(p, pos, lane);
+    const RopeLane rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
+    // Head of this row group in pass ps: h0 + 4 * ps.
+    const int hbase = hb * kHeadsPerItem;
+    const int h0 = hbase + g;
+    const uint16_t* src = p.q + t * p.q_st + (int64_t)h0 * p.q_sh;
+    const int64_t src_pass = (int64_t)kRowsPerWave * p.q_sh;
+    uint8_t* dst = p.q_fp8 + (t * p.H + h0) * kRow;
 
-    // Issue every load of the item before any arithmetic.
+    // Every load of the item first: the rows, and the 16 head gates (lane l
+    // of the first row group takes head hbase + l).
+    const bool gate_lane = lane < kHeadsPerItem && hbase + lane < p.H;
+    uint32_t wbits = 0;
+    if (gate_lane) wbits = p.w[t * p.w_st + hbase + lane];
     uint4 raw[kPasses];
-    uint32_t wbits[kPasses];
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-        const int h = hb * kHeadsPerItem + ps * kRowsPerWave + g;
         raw[ps] = make_uint4(0, 0, 0, 0);
-        wbits[ps] = 0;
-        if (h < p.H) {
-            raw[ps] = *reinterpret_cast<const uint4*>(p.q + t * p.q_st + (int64_t)h * p.q_sh + 8 * j);
-            if (j == 0) wbits[ps] = p.w[t * p.w_st + h];
-        }
+        if (h0 + ps * kRowsPerWave < p.H) raw[ps] = load_row<LAYOUT>(src + ps * src_pass, j);
     }
 
+    int e[kPasses];
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
-        const int h = hb * kHeadsPerItem + ps * kRowsPerWave + g;
-        float x[8];
-        unpack8(raw[ps], x);
-        if (STYLE == 0) {
-            uint4 pr;
-            pr.x = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw[ps].x);
-            pr.y = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw[ps].y);
-            pr.z = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw[ps].z);
-            pr.w = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw[ps].w);
-            float xp[8];
-            unpack8(pr, xp);
-            if (rl.active) rotate_neox(x, xp, rl);
-        } else {
-            if (rl.active) rotate_interleaved(x, rl);
-        }
-        int e;
-        const uint2 codes = quantize8(x, e);
-        if (h < p.H) {
-            const int64_t row = t * p.H + h;
-            *reinterpret_cast<uint2*>(p.q_fp8 + row * kRow + 8 * j) = codes;
-            if (j == 0) {
-                const float sc = exp2_int(e);
-                const float ws = __uint_as_float(wbits[ps] << 16) * p.weight_scale;
-                p.w_out[row] = ws * sc;
-                if (p.q_scale) p.q_scale[row] = sc;
-            }
-        }
+        float y[8];
+        rope_packed_row<STYLE, LAYOUT>(raw[ps], y, rl);
+        e[ps] = scale_exponent(row_max_bits(lane_amax_bits(y)));
+        const uint2 codes = encode8(y, exp2_int(e[ps]));
+        if (h0 + ps * kRowsPerWave < p.H) store_row<LAYOUT>(dst + ps * (kRowsPerWave * kRow), j, codes);
+    }
+
+    // Head gate of head hbase + l on lane l: its exponent was computed in pass
+    // l / 4 by row group l % 4.
+    const int src_addr = ((lane & 3) << 4) << 2;
+    int el = 0;
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+        const int v = __builtin_amdgcn_ds_bpermute(src_addr, e[ps]);
+        if ((lane >> 2) == ps) el = v;
+    }
+    if (gate_lane) {
+        const int64_t row = t * p.H + hbase + lane;
+        const float sc = exp2_int(el);
+        const float ws = __uint_as_float(wbits << 16) * p.weight_scale;
+        p.w_out[row] = ws * sc;
+        if (p.q_scale) p.q_scale[row] = sc;
     }
 }
 
-template <int STYLE>
+template <int STYLE, int LAYOUT>
 __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int lane) {
     const int g = lane >> 4;
     const int j = lane & (kLanesPerRow - 1);
@@ -257,17 +440,14 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
     uint4 raw = make_uint4(0, 0, 0, 0);
     int64_t pos = 0, slot = -1;
     if (valid) {
-        raw = *reinterpret_cast<const uint4*>(p.k + t * p.k_st + 8 * j);
+        raw = load_row<LAYOUT>(p.k + t * p.k_st, j);
         pos = clamp_position(p.k_pos[t], p.P);
         slot = p.loc[t];
     }
-    const RopeLane rl = rope_lane<STYLE>(p, pos, lane);
-    const float4 g0 = reinterpret_cast<const float4*>(p.gamma)[2 * j];
-    const float4 g1 = reinterpret_cast<const float4*>(p.gamma)[2 * j + 1];
-    const float4 b0 = reinterpret_cast<const float4*>(p.beta)[2 * j];
-    const float4 b1 = reinterpret_cast<const float4*>(p.beta)[2 * j + 1];
-    const float gam[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float bet[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    const RopeLane rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
+    float gam[8], bet[8];
+    load_params<LAYOUT>(p.gamma, j, gam);
+    load_params<LAYOUT>(p.beta, j, bet);
 
     float x[8];
     unpack8(raw, x);
@@ -295,41 +475,46 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
         n[m] = dg + bet[m];
     }
 
-    if (STYLE == 0) {
-        float np[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            np[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(rl.partner_addr, __float_as_int(n[m])));
-        if (rl.active) rotate_neox(n, np, rl);
-    } else {
-        if (rl.active) rotate_interleaved(n, rl);
-    }
-    int e;
-    const uint2 codes = quantize8(n, e);
+    rope_row<STYLE, LAYOUT>(n, rl);
+    const int e = scale_exponent(row_max_bits(lane_amax_bits(n)));
+    const uint2 codes = encode8(n, exp2_int(e));
     if (valid && slot >= 0 && slot < p.S) {
-        *reinterpret_cast<uint2*>(p.k_cache + slot * p.k_row_stride + 8 * j) = codes;
+        store_row<LAYOUT>(p.k_cache + slot * p.k_row_stride, j, codes);
         if (j == 0) p.k_scale[slot] = exp2_int(e);
     }
 }
 
-template <int STYLE>
+template <int STYLE, int LAYOUT>
 __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int waves = (int)(blockDim.x >> 6);
-    if ((int)blockIdx.x < p.k_blocks) {
+    const int64_t nblocks = gridDim.x;
+    const int64_t b = blockIdx.x;
+    const int64_t nq = nblocks - p.k_blocks;
+#if DSAIDX_K_PLACEMENT == 2
+    const int64_t k_before = b * p.k_blocks / nblocks;
+    const bool is_key = (b + 1) * p.k_blocks / nblocks > k_before;
+    const int64_t kb = k_before, qb = b - k_before;
+#elif DSAIDX_K_PLACEMENT == 1
+    const bool is_key = b >= nq;
+    const int64_t kb = b - nq, qb = b;
+#else
+    const bool is_key = b < p.k_blocks;
+    const int64_t kb = b, qb = b - p.k_blocks;
+#endif
+    if (is_key) {
         const int64_t stride = (int64_t)p.k_blocks * waves;
-        for (int64_t it = (int64_t)blockIdx.x * waves + wave; it < p.k_items; it += stride)
-            key_item<STYLE>(p, it, lane);
+        for (int64_t it = kb * waves + wave; it < p.k_items; it += stride)
+            key_item<STYLE, LAYOUT>(p, it, lane);
     } else {
-        const int64_t qb = (int64_t)blockIdx.x - p.k_blocks;
-        const int64_t stride = ((int64_t)gridDim.x - p.k_blocks) * waves;
+        const int64_t stride = nq * waves;
         for (int64_t it = qb * waves + wave; it < p.q_items; it += stride)
-            query_item<STYLE>(p, it, lane);
+            query_item<STYLE, LAYOUT>(p, it, lane);
     }
 }
 
-// Eight consecutive values per lane through the same encode8 as the kernels.
+// Eight consecutive values per lane through the kernels' encoder (scale 1).
 __global__ __launch_bounds__(256) void fp8_encode_selftest_kernel(const float* in, uint8_t* out,
                                                                   int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
@@ -338,7 +523,7 @@ __global__ __launch_bounds__(256) void fp8_encode_selftest_kernel(const float* i
         float v[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) v[m] = base + m < n ? in[base + m] : 0.0f;
-        const uint2 c = encode8(v);
+        const uint2 c = encode8(v, 1.0f);
         if (base + 8 <= n) {
             *reinterpret_cast<uint2*>(out + base) = c;
         } else {
@@ -361,8 +546,13 @@ hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned b
                        hipStream_t stream) {
     PrepParams copy = p;
     void* args[] = {&copy};
-    const void* fn = style == 0 ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0>)
-                                : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1>);
+    const void* fn;
+    if (style == 1)
+        fn = reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1, kSplit>);
+    else if (p.R <= 64)
+        fn = reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kSplit>);
+    else
+        fn = reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kContig>);
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream);
 }
 
