@@ -62,7 +62,7 @@ def recorded_traffic(expected_hash: str):
 class Case:
     """Device buffers of one workload for the fused call (inputs copied once)."""
 
-    def __init__(self, wl, torch, R):
+    def __init__(self, wl, torch, R, k_flags=0, page_size=0):
         import numpy as np
         self.wl = wl
         T, H = wl.T, wl.H
@@ -79,11 +79,16 @@ class Case:
         self.beta = torch.from_numpy(wl.beta).cuda()
         self.q_fp8 = torch.empty((T, H, 128), dtype=torch.uint8, device="cuda")
         self.w_out = torch.empty((T, H), dtype=torch.float32, device="cuda")
-        self.k_cache = torch.zeros((wl.num_slots, 128), dtype=torch.uint8, device="cuda")
-        self.k_scale = torch.zeros((wl.num_slots,), dtype=torch.float32, device="cuda")
+        if k_flags & R.DSAIDX_K_PAGED_CACHE:
+            self.k_cache = torch.zeros((wl.num_slots * (128 + 4),), dtype=torch.uint8, device="cuda")
+            self.k_scale = None
+        else:
+            self.k_cache = torch.zeros((wl.num_slots, 128), dtype=torch.uint8, device="cuda")
+            self.k_scale = torch.zeros((wl.num_slots,), dtype=torch.float32, device="cuda")
         self.qa = R.q_args(self.q, self.w, self.pos, self.q_fp8, self.w_out)
         self.ka = R.k_args(self.k, self.gamma, self.beta, wl.eps, self.pos, self.loc,
-                           self.k_cache, self.k_scale)
+                           self.k_cache, self.k_scale, flags=k_flags, page_size=page_size,
+                           num_slots=wl.num_slots)
         self.rope = R.rope_args(self.cos, self.sin, wl.rope_dim, wl.style)
 
 
@@ -225,6 +230,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
+        log("secondary measurements")
         extras = {}
         # decode batch, 64 tokens: back-to-back calls and graph replay
         wl1 = W.named(1)
@@ -245,7 +251,18 @@ def main():
         ms2k = time_graph(torch, lambda: R.dsaidx_k_only_prepare_store(c2.ka, c2.rope), 100, 10)
         extras["decode_large_interleaved_T512"] = {"us_per_call_fused_graph": ms2 * 1e3,
                                                    "us_per_call_k_only_graph": ms2k * 1e3}
-        del c1, c2
+        c2b = Case(wl2, torch, R, k_flags=R.DSAIDX_K_BF16_INTERMEDIATE)
+        ms2b = time_graph(torch, lambda: R.dsaidx_k_only_prepare_store(c2b.ka, c2b.rope), 100, 10)
+        extras["decode_large_interleaved_T512"]["us_per_call_k_only_bf16_writer_graph"] = ms2b * 1e3
+        del c1, c2, c2b
+        # the same long prefill into the page-interleaved index-K cache (64-slot pages)
+        cp = Case(wl, torch, R, k_flags=R.DSAIDX_K_PAGED_CACHE, page_size=64)
+        msp = time_calls(torch, lambda: R.dsaidx_qk_fused(cp.qa, cp.ka, cp.rope), 50, 5)
+        extras["long_prefill_T65536_paged_cache"] = {
+            "us_per_call": msp * 1e3, "achieved_GBps": bytes_call / (msp * 1e-3) / 1e9,
+            "frac_of_peak": bytes_call / (msp * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del cp
+        torch.cuda.empty_cache()
         # 8192-token prefill chunk: 4 rotating buffer sets (> 800 MB) so no
         # step finds its inputs in the last-level cache
         wl3 = W.named(3)

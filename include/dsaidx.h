@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DSAIDX_ABI_VERSION 1
+#define DSAIDX_ABI_VERSION 2
 #define DSAIDX_HEAD_DIM 128 /* width of every head vector and K row */
 
 typedef struct ihipStream_t* dsaidx_stream_t; /* the same type as hipStream_t */
@@ -138,6 +138,25 @@ typedef struct dsaidx_q_args {
     float* q_scale_out;
 } dsaidx_q_args;
 
+/* dsaidx_k_args.flags bits.
+ *
+ * DSAIDX_K_BF16_INTERMEDIATE: the other K-cache writer of [sglang-fuse]
+ *   Accuracy -- the LayerNorm output and the RoPE output are each rounded to
+ *   bf16 (nearest, ties to even) before quantisation, instead of going
+ *   fp32 -> fp8 in one step.  Codes then differ from the default writer only
+ *   near fp8 midpoints (and where the rotation cancels); scales normally agree.
+ *
+ * DSAIDX_K_PAGED_CACHE: the page-interleaved index-K cache ([sglang-fuse]
+ *   Checklist tests two paged layouts without defining them; this is the
+ *   second one).  k_cache holds num_slots / page_size pages of
+ *   page_size * 132 bytes: the page_size 128-byte code rows first, then the
+ *   page_size fp32 scales.  Slot s lives in page s / page_size at offset
+ *   o = s % page_size: codes at page + 128 * o, scale at
+ *   page + 128 * page_size + 4 * o.  k_cache_row_stride and k_scale are unused
+ *   (k_scale may be NULL). */
+#define DSAIDX_K_BF16_INTERMEDIATE 0x1
+#define DSAIDX_K_PAGED_CACHE 0x2
+
 /* Key side ([sglang-fuse] Motivation and Modifications: fp32 LayerNorm with
  * fp32 params, the index-K cache write at the sliced out_cache_loc).
  *   k                  bf16 bits [T, 128]: row t at k + t*k_stride_t; 16-byte aligned;
@@ -145,15 +164,17 @@ typedef struct dsaidx_q_args {
  *                      wider GEMM output is allowed)
  *   ln_gamma, ln_beta  fp32 [128], 16-byte aligned
  *   ln_eps             > 0, finite
- *   flags              must be 0 (reserved)
+ *   flags              0, or DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_PAGED_CACHE bits
  *   positions          int64 [T], 8-byte aligned
  *   out_cache_loc      int64 [T] slot per token, 8-byte aligned
  *   num_tokens         T >= 0
  *   k_cache            in/out: E4M3FN rows; slot s at k_cache + s*k_cache_row_stride,
- *                      codes in its first 128 bytes; 8-byte aligned
- *   k_cache_row_stride bytes, >= 128 and a multiple of 8
- *   k_scale            in/out: fp32 [num_slots], 4-byte aligned
- *   num_slots          S >= 1 */
+ *                      codes in its first 128 bytes (planar layout), or the pages of
+ *                      DSAIDX_K_PAGED_CACHE; 8-byte aligned
+ *   k_cache_row_stride planar: bytes, >= 128 and a multiple of 8
+ *   k_scale            planar: in/out fp32 [num_slots], 4-byte aligned
+ *   num_slots          S >= 1 (paged: a multiple of page_size)
+ *   page_size          paged: slots per page, even, in [2, 2^20]; ignored otherwise */
 typedef struct dsaidx_k_args {
     const uint16_t* k;
     int64_t k_stride_t;
@@ -168,6 +189,7 @@ typedef struct dsaidx_k_args {
     int64_t k_cache_row_stride;
     float* k_scale;
     int64_t num_slots;
+    int64_t page_size;
 } dsaidx_k_args;
 
 /* Query RoPE + fp8/ue8m0 quantisation + head-gate fold: the fused-Q launch of

@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_k.argtypes = [P, i64, P, P, f32, P, P, i64,
                                P, P, i64, i64, i32, i32, i32, P, i64, P, i64, i32]
         L.oracle_k.restype = i32
+        L.oracle_k_paged.argtypes = [P, i64, P, P, f32, P, P, i64,
+                                     P, P, i64, i64, i32, i32, i32, P, i64, i64, i32]
+        L.oracle_k_paged.restype = i32
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = i32
         _lib = L
@@ -204,3 +207,24 @@ def k_side(k, gamma, beta, eps, positions, out_cache_loc, cos, sin, k_cache, k_s
                         _p(k_cache), row_stride, _p(k_scale), S, nthreads)
     if rc != 0:
         raise ValueError("oracle_k: position out of range (rc=%d)" % rc)
+
+
+def k_side_paged(k, gamma, beta, eps, positions, out_cache_loc, cos, sin, cache, page_size,
+                 num_slots, rope_dim=64, style=NEOX, bf16_mode=0, nthreads=0):
+    """Writes into cache (uint8, num_slots * 132 bytes, page-interleaved) in place."""
+    T, D = k.shape
+    assert D == ROW and k.dtype == np.uint16
+    k_st, k_si = _elem_strides(k)
+    assert k_si == 1
+    assert cache.dtype == np.uint8 and cache.flags.c_contiguous
+    assert cache.size == num_slots * (ROW + 4)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    positions = np.ascontiguousarray(positions, dtype=np.int64)
+    loc = np.ascontiguousarray(out_cache_loc, dtype=np.int64)
+    rs, P = rope_tables(cos, sin)
+    rc = lib().oracle_k_paged(_p(k), k_st, _p(gamma), _p(beta), float(eps), _p(positions), _p(loc),
+                              T, _p(cos), _p(sin), rs, P, rope_dim, style, bf16_mode,
+                              _p(cache), page_size, num_slots, nthreads)
+    if rc != 0:
+        raise ValueError("oracle_k_paged failed (rc=%d)" % rc)

@@ -333,3 +333,41 @@ int oracle_k(const uint16_t* k, int64_t k_st,
     free(e);
     return rc;
 }
+
+/* K side into the page-interleaved cache: num_slots / page_size pages of
+ * page_size * 132 bytes, each holding its page_size 128-byte code rows and
+ * then its page_size fp32 scales.  Slot s is in page s / page_size at offset
+ * s % page_size.  Slots outside [0, S) are skipped. */
+int oracle_k_paged(const uint16_t* k, int64_t k_st,
+                   const float* gamma, const float* beta, float eps,
+                   const int64_t* pos, const int64_t* loc, int64_t T,
+                   const float* cos_t, const float* sin_t, int64_t rs, int64_t P,
+                   int R, int style, int bf16_mode,
+                   uint8_t* cache, int64_t page_size, int64_t S, int nthreads) {
+    if (T <= 0) return 0;
+    if (page_size <= 0 || S % page_size != 0) return -3;
+    float* y = (float*)malloc((size_t)T * ROW * sizeof(float));
+    int32_t* e = (int32_t*)malloc((size_t)T * sizeof(int32_t));
+    if (!y || !e) {
+        free(y);
+        free(e);
+        return -2;
+    }
+    int rc = oracle_k_values(k, k_st, gamma, beta, eps, pos, T, cos_t, sin_t, rs, P,
+                             R, style, bf16_mode, y, e, nthreads);
+    if (rc == 0) {
+        const int64_t page_bytes = page_size * (ROW + (int64_t)sizeof(float));
+        for (int64_t t = 0; t < T; t++) {
+            int64_t slot = loc[t];
+            if (slot < 0 || slot >= S) continue;
+            uint8_t* page = cache + (slot / page_size) * page_bytes;
+            int64_t off = slot % page_size;
+            encode_row(y + t * ROW, e[t], page + off * ROW);
+            float sc = ldexpf(1.0f, e[t]);
+            memcpy(page + page_size * ROW + off * (int64_t)sizeof(float), &sc, sizeof sc);
+        }
+    }
+    free(y);
+    free(e);
+    return rc;
+}

@@ -84,6 +84,17 @@ int oracle_k(const uint16_t* k, int64_t k_st,
              uint8_t* k_cache, int64_t row_stride, float* k_scale, int64_t S,
              int nthreads);
 
+/* K side into the page-interleaved cache: num_slots / page_size pages of
+ * page_size * 132 bytes -- the page's page_size 128-byte code rows, then its
+ * page_size fp32 scales.  Slot s: page s / page_size, offset s % page_size.
+ * Returns 0, -1 on a bad position, -3 if page_size does not divide S. */
+int oracle_k_paged(const uint16_t* k, int64_t k_st,
+                   const float* gamma, const float* beta, float eps,
+                   const int64_t* pos, const int64_t* loc, int64_t T,
+                   const float* cos_t, const float* sin_t, int64_t rs, int64_t P,
+                   int R, int style, int bf16_mode,
+                   uint8_t* cache, int64_t page_size, int64_t S, int nthreads);
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_max_threads(void);
 

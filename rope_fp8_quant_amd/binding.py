@@ -21,6 +21,9 @@ DSAIDX_ERR_UNSUPPORTED = 2
 DSAIDX_ERR_HIP = 3
 DSAIDX_ROPE_NEOX = 0
 DSAIDX_ROPE_INTERLEAVED = 1
+DSAIDX_K_BF16_INTERMEDIATE = 0x1
+DSAIDX_K_PAGED_CACHE = 0x2
+PAGED_SLOT_BYTES = ROW + 4   # one code row and one fp32 scale per slot
 EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaidx_qk_fused",
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
             "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest")
@@ -54,7 +57,7 @@ class DsaidxKArgs(ctypes.Structure):
                 ("positions", ctypes.c_void_p), ("out_cache_loc", ctypes.c_void_p),
                 ("num_tokens", ctypes.c_int64), ("k_cache", ctypes.c_void_p),
                 ("k_cache_row_stride", ctypes.c_int64), ("k_scale", ctypes.c_void_p),
-                ("num_slots", ctypes.c_int64)]
+                ("num_slots", ctypes.c_int64), ("page_size", ctypes.c_int64)]
 
 
 _lib = None
@@ -211,10 +214,16 @@ def q_args(q, weights, positions, q_fp8, weights_out, q_scale_out=None,
 
 
 def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cache,
-           k_scale) -> DsaidxKArgs:
+           k_scale=None, flags: int = 0, page_size: int = 0, num_slots=None) -> DsaidxKArgs:
     """k: bf16 [T, 128] (unit inner stride); ln_gamma/ln_beta float32 [128];
-    positions/out_cache_loc int64 [T]; k_cache 1-byte [S, >=128] (unit inner
-    stride; codes go to the first 128 bytes of each row); k_scale float32 [S]."""
+    positions/out_cache_loc int64 [T].
+
+    Planar cache (default): k_cache 1-byte [S, >=128] (unit inner stride;
+    codes go to the first 128 bytes of each row), k_scale float32 [S].
+    Paged cache (flags has DSAIDX_K_PAGED_CACHE): k_cache a contiguous 1-byte
+    tensor of num_slots * 132 bytes holding pages of page_size slots (code
+    rows, then fp32 scales); k_scale unused.  DSAIDX_K_BF16_INTERMEDIATE
+    selects the bf16-intermediate writer."""
     import torch
     _need(k.dtype == torch.bfloat16 and k.dim() == 2 and k.shape[1] == ROW and k.stride(1) == 1,
           "k must be bf16 [T, 128] with unit inner stride")
@@ -225,11 +234,19 @@ def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cach
     for name, t in (("positions", positions), ("out_cache_loc", out_cache_loc)):
         _need(t.dtype == torch.int64 and t.numel() == T and t.is_contiguous(),
               "%s must be contiguous int64 [T]" % name)
-    _need(k_cache.element_size() == 1 and k_cache.dim() == 2 and k_cache.shape[1] >= ROW
-          and k_cache.stride(1) == 1, "k_cache must be a 1-byte [S, >=128] tensor")
-    S = k_cache.shape[0]
-    _need(k_scale.dtype == torch.float32 and k_scale.numel() == S and k_scale.is_contiguous(),
-          "k_scale must be contiguous float32 [S]")
-    return DsaidxKArgs(_ptr(k), k.stride(0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps), 0,
-                       _ptr(positions), _ptr(out_cache_loc), T, _ptr(k_cache), k_cache.stride(0),
-                       _ptr(k_scale), S)
+    _need(k_cache.element_size() == 1, "k_cache must be a 1-byte tensor")
+    if flags & DSAIDX_K_PAGED_CACHE:
+        _need(k_cache.is_contiguous(), "a paged k_cache must be contiguous")
+        S = int(num_slots) if num_slots is not None else k_cache.numel() // PAGED_SLOT_BYTES
+        _need(k_cache.numel() >= S * PAGED_SLOT_BYTES, "paged k_cache smaller than num_slots * 132")
+        row_stride, scale_ptr = 0, _ptr(k_scale)
+    else:
+        _need(k_cache.dim() == 2 and k_cache.shape[1] >= ROW and k_cache.stride(1) == 1,
+              "k_cache must be a 1-byte [S, >=128] tensor")
+        S = k_cache.shape[0]
+        _need(k_scale is not None and k_scale.dtype == torch.float32 and k_scale.numel() == S
+              and k_scale.is_contiguous(), "k_scale must be contiguous float32 [S]")
+        row_stride, scale_ptr = k_cache.stride(0), _ptr(k_scale)
+    return DsaidxKArgs(_ptr(k), k.stride(0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps),
+                       int(flags), _ptr(positions), _ptr(out_cache_loc), T, _ptr(k_cache),
+                       row_stride, scale_ptr, S, int(page_size))

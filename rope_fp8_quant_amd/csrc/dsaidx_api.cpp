@@ -7,6 +7,9 @@
 
 #include "dsaidx_internal.h"
 
+static_assert(dsaidx::kKeyBf16Intermediate == DSAIDX_K_BF16_INTERMEDIATE, "flag bits");
+static_assert(dsaidx::kKeyPagedCache == DSAIDX_K_PAGED_CACHE, "flag bits");
+
 namespace {
 
 using dsaidx::PrepParams;
@@ -58,19 +61,25 @@ dsaidx_status check_q(const dsaidx_q_args* q) {
 }
 
 dsaidx_status check_k(const dsaidx_k_args* k) {
-    if (!k->k || !k->ln_gamma || !k->ln_beta || !k->positions || !k->out_cache_loc ||
-        !k->k_cache || !k->k_scale)
+    if (!k->k || !k->ln_gamma || !k->ln_beta || !k->positions || !k->out_cache_loc || !k->k_cache)
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (!aligned(k->k, 16) || !aligned(k->ln_gamma, 16) || !aligned(k->ln_beta, 16) ||
-        !aligned(k->positions, 8) || !aligned(k->out_cache_loc, 8) || !aligned(k->k_cache, 8) ||
-        !aligned(k->k_scale, 4))
+        !aligned(k->positions, 8) || !aligned(k->out_cache_loc, 8) || !aligned(k->k_cache, 8))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (k->k_stride_t < dsaidx::kRow || k->k_stride_t % 8 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (!(k->ln_eps > 0.0f) || !std::isfinite(k->ln_eps)) return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (k->flags != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (k->k_cache_row_stride < dsaidx::kRow || k->k_cache_row_stride % 8 != 0)
+    if (k->flags & ~(DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_PAGED_CACHE))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (k->num_slots < 1) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->flags & DSAIDX_K_PAGED_CACHE) {
+        if (k->page_size < 2 || k->page_size > (1 << 20) || k->page_size % 2 != 0 ||
+            k->num_slots % k->page_size != 0)
+            return DSAIDX_ERR_INVALID_ARGUMENT;
+    } else {
+        if (!k->k_scale || !aligned(k->k_scale, 4)) return DSAIDX_ERR_INVALID_ARGUMENT;
+        if (k->k_cache_row_stride < dsaidx::kRow || k->k_cache_row_stride % 8 != 0)
+            return DSAIDX_ERR_INVALID_ARGUMENT;
+    }
     return DSAIDX_OK;
 }
 
@@ -111,6 +120,8 @@ void fill_k(PrepParams& p, const dsaidx_k_args& k) {
     p.k_row_stride = k.k_cache_row_stride;
     p.k_scale = k.k_scale;
     p.S = k.num_slots;
+    p.k_flags = k.flags;
+    p.page_size = (k.flags & DSAIDX_K_PAGED_CACHE) ? k.page_size : 0;
     p.k_items = (k.num_tokens + dsaidx::kTokensPerKItem - 1) / dsaidx::kTokensPerKItem;
     p.T = k.num_tokens;
 }

@@ -14,6 +14,9 @@ constexpr int kRowsPerWave = 4;     // 64 lanes / 16
 #endif
 constexpr int kHeadsPerItem = DSAIDX_HEADS_PER_ITEM;  // query heads per wavefront work item
 constexpr int kTokensPerKItem = 4;  // key rows per wavefront work item
+constexpr int32_t kKeyBf16Intermediate = 0x1;  // DSAIDX_K_BF16_INTERMEDIATE
+constexpr int32_t kKeyPagedCache = 0x2;        // DSAIDX_K_PAGED_CACHE
+constexpr int kPagedScaleBytes = 4;            // fp32 scale per slot in a paged cache
 
 // Everything one dispatch needs.  k_blocks workgroups run key work items and
 // the others query work items (which ones: see the kernel); either set may be
@@ -41,9 +44,11 @@ struct PrepParams {
     const int64_t* k_pos;
     const int64_t* loc;
     uint8_t* k_cache;
-    int64_t k_row_stride;  // bytes
-    float* k_scale;
+    int64_t k_row_stride;  // bytes (planar cache)
+    float* k_scale;        // planar cache
     int64_t S;
+    int64_t page_size;     // paged cache: slots per page (0 = planar)
+    int32_t k_flags;       // DSAIDX_K_* bits
     int64_t k_items;       // ceil(T / 4) (0 when the dispatch has no key work)
     int64_t T;
     float eps;

@@ -204,6 +204,13 @@ __device__ __forceinline__ int scale_exponent(uint32_t amax_bits) {
     return (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
 }
 
+// fp32 -> nearest bf16 (ties to even), kept as fp32; finite inputs.
+__device__ __forceinline__ float round_bf16(float v) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return __uint_as_float(u & 0xFFFF0000u);
+}
+
 __device__ __forceinline__ float exp2_int(int e) {
     return __uint_as_float((uint32_t)(127 + e) << 23);
 }
@@ -475,12 +482,34 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
         n[m] = dg + bet[m];
     }
 
+    // The bf16-intermediate writer rounds the LayerNorm output and the RoPE
+    // output to bf16 ([sglang-fuse] Accuracy, the unfused K-cache writer).
+    const bool bf16_steps = (p.k_flags & kKeyBf16Intermediate) != 0;
+    if (bf16_steps) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) n[m] = round_bf16(n[m]);
+    }
     rope_row<STYLE, LAYOUT>(n, rl);
+    if (bf16_steps) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) n[m] = round_bf16(n[m]);
+    }
     const int e = scale_exponent(row_max_bits(lane_amax_bits(n)));
     const uint2 codes = encode8(n, exp2_int(e));
     if (valid && slot >= 0 && slot < p.S) {
-        store_row<LAYOUT>(p.k_cache + slot * p.k_row_stride, j, codes);
-        if (j == 0) p.k_scale[slot] = exp2_int(e);
+        if (p.page_size > 0) {
+            // page-interleaved cache: [page_size code rows | page_size fp32 scales]
+            const int64_t page = slot / p.page_size;
+            const int64_t off = slot - page * p.page_size;
+            uint8_t* base = p.k_cache + page * p.page_size * (kRow + kPagedScaleBytes);
+            store_row<LAYOUT>(base + off * kRow, j, codes);
+            if (j == 0)
+                *reinterpret_cast<float*>(base + p.page_size * kRow + off * kPagedScaleBytes) =
+                    exp2_int(e);
+        } else {
+            store_row<LAYOUT>(p.k_cache + slot * p.k_row_stride, j, codes);
+            if (j == 0) p.k_scale[slot] = exp2_int(e);
+        }
     }
 }
 

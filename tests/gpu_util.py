@@ -37,11 +37,14 @@ class DeviceCase:
                    the layout of a fused wk/weights projection output
     combined_table cos/sin as the two halves of one [P, rope_dim] buffer
     cache_row_pad  extra bytes after each 128-byte cache row
+    k_flags        DSAIDX_K_* bits (bf16-intermediate writer, paged cache)
+    page_size      slots per page of the paged cache
     """
 
     def __init__(self, wl: W.Workload, q_head_pad=0, gemm_layout=False, combined_table=False,
-                 cache_row_pad=0, q_scale_out=True):
+                 cache_row_pad=0, q_scale_out=True, k_flags=0, page_size=0):
         self.wl = wl
+        self.k_flags, self.page_size = k_flags, page_size
         T, H = wl.T, wl.H
         if q_head_pad:
             buf = torch.zeros((T, H, ROW + q_head_pad), dtype=torch.bfloat16, device="cuda")
@@ -69,11 +72,18 @@ class DeviceCase:
         self.w_out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
         self.q_scale = (torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
                         if q_scale_out else None)
-        cache = torch.full((wl.num_slots, ROW + cache_row_pad), SENTINEL, dtype=torch.uint8,
-                           device="cuda")
-        self.cache_full = cache
-        self.k_cache = cache[:, :ROW]
-        self.k_scale = torch.full((wl.num_slots,), float("nan"), dtype=torch.float32, device="cuda")
+        if k_flags & R.DSAIDX_K_PAGED_CACHE:
+            self.cache_full = torch.full((wl.num_slots * (ROW + 4),), SENTINEL, dtype=torch.uint8,
+                                         device="cuda")
+            self.k_cache = self.cache_full
+            self.k_scale = None
+        else:
+            cache = torch.full((wl.num_slots, ROW + cache_row_pad), SENTINEL, dtype=torch.uint8,
+                               device="cuda")
+            self.cache_full = cache
+            self.k_cache = cache[:, :ROW]
+            self.k_scale = torch.full((wl.num_slots,), float("nan"), dtype=torch.float32,
+                                      device="cuda")
 
     def rope(self):
         return R.rope_args(self.cos, self.sin, self.wl.rope_dim, self.wl.style)
@@ -84,7 +94,8 @@ class DeviceCase:
 
     def ka(self):
         return R.k_args(self.k, self.gamma, self.beta, self.wl.eps, self.positions, self.loc,
-                        self.k_cache, self.k_scale)
+                        self.k_cache, self.k_scale, flags=self.k_flags, page_size=self.page_size,
+                        num_slots=self.wl.num_slots)
 
     def run(self, entry: str):
         if entry == "fused":
@@ -104,7 +115,9 @@ class DeviceCase:
 
     def host(self):
         out = dict(q_fp8=self.q_fp8.cpu().numpy(), w_out=self.w_out.cpu().numpy(),
-                   k_cache=self.cache_full.cpu().numpy(), k_scale=self.k_scale.cpu().numpy())
+                   k_cache=self.cache_full.cpu().numpy())
+        if self.k_scale is not None:
+            out["k_scale"] = self.k_scale.cpu().numpy()
         if self.q_scale is not None:
             out["q_scale"] = self.q_scale.cpu().numpy()
         return out
@@ -119,12 +132,28 @@ def oracle_q(wl: W.Workload, tokens=None):
     return oracle.q_side(q, w, pos, wl.cos, wl.sin, wl.rope_dim, wl.style, wl.weight_scale)
 
 
-def oracle_k(wl: W.Workload, cache_row_pad=0):
+def oracle_k(wl: W.Workload, cache_row_pad=0, k_flags=0, page_size=0):
+    bf16_mode = 1 if k_flags & R.DSAIDX_K_BF16_INTERMEDIATE else 0
+    if k_flags & R.DSAIDX_K_PAGED_CACHE:
+        buf = np.full(wl.num_slots * (ROW + 4), SENTINEL, np.uint8)
+        oracle.k_side_paged(wl.k, wl.gamma, wl.beta, wl.eps, wl.positions, wl.out_cache_loc,
+                            wl.cos, wl.sin, buf, page_size, wl.num_slots, wl.rope_dim, wl.style,
+                            bf16_mode)
+        return split_paged(buf, page_size, wl.num_slots)
     kc = np.full((wl.num_slots, ROW + cache_row_pad), SENTINEL, np.uint8)
     ks = np.full(wl.num_slots, np.nan, np.float32)
     oracle.k_side(wl.k, wl.gamma, wl.beta, wl.eps, wl.positions, wl.out_cache_loc, wl.cos,
-                  wl.sin, kc[:, :ROW], ks, wl.rope_dim, wl.style)
+                  wl.sin, kc[:, :ROW], ks, wl.rope_dim, wl.style, bf16_mode)
     return kc, ks
+
+
+def split_paged(buf: np.ndarray, page_size: int, num_slots: int):
+    """Code rows [S, 128] and scales [S] of a page-interleaved cache buffer
+    (pages of page_size code rows followed by page_size fp32 scales)."""
+    pages = buf.reshape(num_slots // page_size, page_size * (ROW + 4))
+    codes = pages[:, :page_size * ROW].reshape(num_slots, ROW)
+    scales = np.ascontiguousarray(pages[:, page_size * ROW:]).view(np.float32).reshape(num_slots)
+    return codes, scales
 
 
 # ---------------------------------------------------------- comparison ----
@@ -154,20 +183,29 @@ def compare_rel(got: np.ndarray, want: np.ndarray, what: str, rel=1e-6):
 
 
 def check_q(out: dict, wl: W.Workload, report: dict, tokens=None):
+    """Query side.  Beyond the acceptance rules, the query arithmetic is fixed
+    op for op (bf16 -> fp32 exact, separately rounded products and sums, a
+    power-of-two scale), so the codes and folded weights must match the oracle
+    byte for byte."""
     q8, wo, qs = oracle_q(wl, tokens)
     got_q8 = out["q_fp8"] if tokens is None else out["q_fp8"][tokens]
     got_wo = out["w_out"] if tokens is None else out["w_out"][tokens]
     compare_codes(got_q8, q8, "q_fp8", report)
     compare_rel(got_wo, wo, "weights_out")
     report["weights_out_bit_exact"] = bool(np.array_equal(got_wo.view(np.uint32), wo.view(np.uint32)))
+    assert report["q_fp8"]["bytes_differ"] == 0, report["q_fp8"]
+    assert report["weights_out_bit_exact"]
     if "q_scale" in out:
         got_qs = out["q_scale"] if tokens is None else out["q_scale"][tokens]
         compare_exact_f32(got_qs, qs, "q_scale")
 
 
-def check_k(out: dict, wl: W.Workload, report: dict, cache_row_pad=0):
-    kc, ks = oracle_k(wl, cache_row_pad)
-    got_kc, got_ks = out["k_cache"], out["k_scale"]
+def check_k(out: dict, wl: W.Workload, report: dict, cache_row_pad=0, k_flags=0, page_size=0):
+    kc, ks = oracle_k(wl, cache_row_pad, k_flags, page_size)
+    if k_flags & R.DSAIDX_K_PAGED_CACHE:
+        got_kc, got_ks = split_paged(out["k_cache"], page_size, wl.num_slots)
+    else:
+        got_kc, got_ks = out["k_cache"], out["k_scale"]
     # slot placement and scales: exact (NaN sentinel compared bitwise)
     compare_exact_f32(got_ks, ks, "k_scale")
     touched = np.zeros(wl.num_slots, bool)

@@ -46,10 +46,10 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_struct_sizes(L):
-    assert B.dsaidx_abi_version() == 1
+    assert B.dsaidx_abi_version() == 2
     assert L.dsaidx_struct_size(0) == ctypes.sizeof(B.DsaidxRope) == 40
     assert L.dsaidx_struct_size(1) == ctypes.sizeof(B.DsaidxQArgs) == 88
-    assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 96
+    assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 104
     assert L.dsaidx_struct_size(7) == 0
 
 
@@ -83,7 +83,7 @@ def good_q(T=1, **kw):
 
 
 def good_k(T=1, **kw):
-    k = B.DsaidxKArgs(FAKE, 128, FAKE, FAKE, 1e-6, 0, FAKE, FAKE, T, FAKE, 128, FAKE, 4096)
+    k = B.DsaidxKArgs(FAKE, 128, FAKE, FAKE, 1e-6, 0, FAKE, FAKE, T, FAKE, 128, FAKE, 4096, 0)
     for k_, v in kw.items():
         setattr(k, k_, v)
     return k
@@ -158,8 +158,12 @@ BAD_K = [dict(k=None), dict(ln_gamma=None), dict(ln_beta=None), dict(positions=N
          dict(k=FAKE + 8), dict(ln_gamma=FAKE + 4), dict(out_cache_loc=FAKE + 4),
          dict(k_cache=FAKE + 4), dict(k_scale=FAKE + 2), dict(num_tokens=-3),
          dict(k_stride_t=64), dict(k_stride_t=130), dict(ln_eps=0.0), dict(ln_eps=-1e-6),
-         dict(ln_eps=float("nan")), dict(ln_eps=float("inf")), dict(flags=1),
-         dict(k_cache_row_stride=120), dict(k_cache_row_stride=132), dict(num_slots=0)]
+         dict(ln_eps=float("nan")), dict(ln_eps=float("inf")), dict(flags=4), dict(flags=-1),
+         dict(k_cache_row_stride=120), dict(k_cache_row_stride=132), dict(num_slots=0),
+         dict(flags=1, k_scale=None),
+         dict(flags=2, page_size=0), dict(flags=2, page_size=1), dict(flags=2, page_size=3),
+         dict(flags=2, page_size=-64), dict(flags=2, page_size=1 << 21),
+         dict(flags=2, page_size=64, num_slots=100), dict(flags=3, page_size=6, num_slots=64)]
 
 
 @pytest.mark.parametrize("kw", BAD_K, ids=lambda d: str(d))

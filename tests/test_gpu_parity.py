@@ -150,16 +150,16 @@ def test_fused_bytes_equal_q_then_k(idx):
 
 def test_long_prefill_full_size_sampled():
     """65536 tokens at positions 196608..262143, one fused dispatch (the
-    benchmark's launch).  Q checked on 2048 sampled tokens (all tokens with a
-    zero row among them), K checked on every token."""
+    benchmark's launch).  Q checked on 2048 random tokens, the first and last
+    64 tokens and every token with a zero row; K checked on every token."""
     wl = named(4)
     c = DeviceCase(wl)
     c.run("fused")
     out = c.host()
     rng = np.random.default_rng(44)
     zt = np.unique(wl.info["zero_q_rows"] // wl.H)
-    tokens = np.unique(np.concatenate([zt, rng.choice(wl.T, 2048 - min(2048, zt.size),
-                                                      replace=False)]))
+    tokens = np.unique(np.concatenate([zt, rng.choice(wl.T, 2048, replace=False),
+                                       np.arange(64), np.arange(wl.T - 64, wl.T)]))
     rep = {"sampled_tokens": int(tokens.size)}
     check_q(out, wl, rep, tokens=tokens)
     check_k(out, wl, rep)
@@ -336,3 +336,52 @@ def test_rows_span_many_grid_strides():
     check_q(out, wl, rep)
     check_k(out, wl, rep)
     log("fused T=20000", rep)
+
+
+# ----------------------------------------- second cache layout, bf16 writer ----
+
+KEY_MODES = [("bf16", R.DSAIDX_K_BF16_INTERMEDIATE, 0),
+             ("paged64", R.DSAIDX_K_PAGED_CACHE, 64),
+             ("paged2_bf16", R.DSAIDX_K_PAGED_CACHE | R.DSAIDX_K_BF16_INTERMEDIATE, 2)]
+
+
+@pytest.mark.parametrize("mode", KEY_MODES, ids=lambda m: m[0])
+@pytest.mark.parametrize("entry", ["fused", "k", "k_only"])
+@pytest.mark.parametrize("idx", [0, 2, 3])
+def test_key_writer_modes(idx, entry, mode):
+    """The bf16-intermediate writer and the page-interleaved cache against the
+    oracle's same modes; the query outputs are unaffected."""
+    name, flags, page = mode
+    wl = named(idx)
+    c = DeviceCase(wl, k_flags=flags, page_size=page)
+    c.run(entry)
+    out = c.host()
+    rep = {}
+    check_k(out, wl, rep, k_flags=flags, page_size=page)
+    if entry == "fused":
+        check_q(out, wl, rep)
+    log("%s %s %s" % (entry, name, wl.name), rep)
+
+
+def test_two_k_cache_writers_on_gpu():
+    """The two-writer comparison of the sglang PR (section Accuracy), with both
+    writers on the GPU, on the 41-token workload: identical scales, and the
+    single-step writer never farther from the fp32 value (the oracle's fp32
+    values).  The count of differing codes is reported (parity unpinned)."""
+    wl = named(0)
+    a = DeviceCase(wl)
+    b = DeviceCase(wl, k_flags=R.DSAIDX_K_BF16_INTERMEDIATE)
+    a.run("k")
+    b.run("k")
+    ha, hb = a.host(), b.host()
+    loc = wl.out_cache_loc
+    assert np.array_equal(ha["k_scale"][loc], hb["k_scale"][loc])
+    c32, c16 = ha["k_cache"][loc], hb["k_cache"][loc]
+    y, e = oracle.k_values(wl.k, wl.gamma, wl.beta, wl.eps, wl.positions, wl.cos, wl.sin)
+    ref = y.astype(np.float64) * np.exp2(-e.astype(np.float64))[:, None]
+    dec = np.array([oracle.fp8_decode(v) for v in range(256)], dtype=np.float64)
+    assert np.all(np.abs(dec[c32] - ref) <= np.abs(dec[c16] - ref))
+    ordv = lambda x: np.where(x & 0x80, -(x & 0x7F).astype(int), (x & 0x7F).astype(int))
+    d = np.abs(ordv(c32) - ordv(c16))
+    log("two K-cache writers (GPU)", dict(differ=int(np.count_nonzero(d)), elements=int(d.size),
+                                           by_one=int(np.count_nonzero(d == 1)), max_steps=int(d.max())))
