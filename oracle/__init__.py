@@ -24,28 +24,31 @@ NEOX = 0
 INTERLEAVED = 1
 
 
-def build(force: bool = True) -> str:
+def build(force: bool = True, sources=None, out_path: str = LIB_PATH) -> str:
     """Compile the oracle with gcc (fp32, no contraction, OpenMP)."""
-    if not force and os.path.exists(LIB_PATH):
-        return LIB_PATH
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    if not force and os.path.exists(out_path):
+        return out_path
+    tmp = out_path + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
-           "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp] + SOURCES + ["-lm"]
+           "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-I" + _HERE,
+           "-o", tmp] + list(sources or SOURCES) + ["-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library.  ORACLE_LIB overrides the path (the mutation tests
+    point it at builds of the oracle with a planted mistake)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("ORACLE_LIB", LIB_PATH)
+        if path == LIB_PATH and not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
         i32 = ctypes.c_int

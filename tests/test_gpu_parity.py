@@ -385,3 +385,113 @@ def test_two_k_cache_writers_on_gpu():
     d = np.abs(ordv(c32) - ordv(c16))
     log("two K-cache writers (GPU)", dict(differ=int(np.count_nonzero(d)), elements=int(d.size),
                                            by_one=int(np.count_nonzero(d == 1)), max_steps=int(d.max())))
+
+
+# ------------------------------------------------ graphs, streams, sizes ----
+
+def test_graph_replays_match_eager_calls():
+    """One fused call captured in a HIP graph and replayed with fresh inputs
+    copied into the captured buffers; every replay equals an eager call on the
+    same inputs (eager work and synchronisation between replays)."""
+    wl = W.make(96, 64, values="sparse_outliers", table_rows=4096, num_slots=1024, seed=31)
+    c = DeviceCase(wl)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        R.dsaidx_qk_fused(c.qa(), c.ka(), c.rope())
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    qa, ka, rope = c.qa(), c.ka(), c.rope()
+    with torch.cuda.graph(g):
+        R.dsaidx_qk_fused(qa, ka, rope)
+    for rep in range(4):
+        other = W.make(96, 64, values="sparse_outliers", table_rows=4096, num_slots=1024,
+                       seed=100 + rep)
+        c.q.copy_(dev_bf16(other.q))
+        c.k.copy_(dev_bf16(other.k))
+        c.weights.copy_(dev_bf16(other.weights))
+        c.positions.copy_(dev(other.positions))
+        c.loc.copy_(dev(other.out_cache_loc))
+        c.gamma.copy_(dev(other.gamma))
+        c.beta.copy_(dev(other.beta))
+        c.k_cache.fill_(SENTINEL)
+        c.k_scale.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = c.host()
+        e = DeviceCase(other)
+        e.run("fused")
+        want = e.host()
+        for key in ("q_fp8", "w_out", "k_cache", "k_scale"):
+            assert np.array_equal(got[key].view(np.uint8), want[key].view(np.uint8)), (rep, key)
+        rep_ = {}
+        check_q(got, other, rep_)
+        check_k(got, other, rep_)
+
+
+def test_concurrent_streams():
+    """Two workloads on two streams at once; each result matches the oracle."""
+    wa = W.make(300, 64, table_rows=4096, num_slots=4096, seed=41)
+    wb = W.make(257, 64, style=W.INTERLEAVED, table_rows=4096, num_slots=4096, seed=42)
+    ca, cb = DeviceCase(wa), DeviceCase(wb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        R.dsaidx_qk_fused(ca.qa(), ca.ka(), ca.rope(), stream=sa)
+        R.dsaidx_qk_fused(cb.qa(), cb.ka(), cb.rope(), stream=sb)
+    torch.cuda.synchronize()
+    for c, wl in ((ca, wa), (cb, wb)):
+        out = c.host()
+        rep = {}
+        check_q(out, wl, rep)
+        check_k(out, wl, rep)
+
+
+def test_offsets_beyond_2_pow_31_elements():
+    """T * H * 128 > 2^31: 270000 tokens x 64 heads (4.4 GB of q).  The inputs
+    tile the 8192-token prefill recipe (token t takes row t % 8192) with
+    positions t % 32768 and slots t; sampled tokens, the first and the last
+    ones are checked against the oracle."""
+    T = 270000
+    base = named(3)
+    src = torch.arange(T, device="cuda") % base.T
+    q = dev_bf16(base.q)[src]
+    k = dev_bf16(base.k)[src]
+    w = dev_bf16(base.weights)[src]
+    pos_np = (np.arange(T) % 32768).astype(np.int64)
+    cos, sin = W.rope_table(32768, 64)
+    S = T + 16
+    loc_np = np.arange(T, dtype=np.int64)
+    q_fp8 = torch.empty((T, 64, ROW), dtype=torch.uint8, device="cuda")
+    w_out = torch.empty((T, 64), dtype=torch.float32, device="cuda")
+    k_cache = torch.full((S, ROW), SENTINEL, dtype=torch.uint8, device="cuda")
+    k_scale = torch.full((S,), float("nan"), dtype=torch.float32, device="cuda")
+    pos, loc = dev(pos_np), dev(loc_np)
+    gcos, gsin = dev(cos), dev(sin)
+    gam, bet = dev(base.gamma), dev(base.beta)
+    R.dsaidx_qk_fused(R.q_args(q, w, pos, q_fp8, w_out),
+                      R.k_args(k, gam, bet, base.eps, pos, loc, k_cache, k_scale),
+                      R.rope_args(gcos, gsin, 64, W.NEOX))
+    torch.cuda.synchronize()
+    del q, k
+    rng = np.random.default_rng(5)
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+                                       rng.choice(T, 256, replace=False)]))
+    rows = tokens % base.T
+    oq8, owo, _ = oracle.q_side(base.q[rows], base.weights[rows], pos_np[tokens], cos, sin)
+    t_dev = torch.from_numpy(tokens).cuda()
+    assert np.array_equal(q_fp8[t_dev].cpu().numpy(), oq8)
+    assert np.array_equal(w_out[t_dev].cpu().numpy().view(np.uint32), owo.view(np.uint32))
+    kc = np.full((len(tokens), ROW), SENTINEL, np.uint8)
+    ks = np.full(len(tokens), np.nan, np.float32)
+    oracle.k_side(base.k[rows], base.gamma, base.beta, base.eps, pos_np[tokens],
+                  np.arange(len(tokens)), cos, sin, kc, ks)
+    got_kc = k_cache[t_dev].cpu().numpy()
+    d = np.abs(got_kc.astype(np.int32) - kc.astype(np.int32))
+    assert np.count_nonzero(got_kc != kc) <= 0.001 * kc.size
+    assert np.array_equal(k_scale[t_dev].cpu().numpy(), ks)
+    assert np.all(k_cache[T:].cpu().numpy() == SENTINEL)
+    log("fused T=270000 (offsets > 2^31)", dict(tokens_checked=int(len(tokens)),
+                                                 k_bytes_differ=int(np.count_nonzero(d))))

@@ -71,6 +71,17 @@ def test_saturation_and_signed_zero(oracle_lib):
     assert oracle_lib.fp8_encode(3 * 2.0 ** -10) == 0x02   # tie between 1 and 2 (x 2^-9)
 
 
+def test_encoder_ties_on_every_binade(oracle_lib):
+    """Every exact midpoint between neighbouring codes, positive and negative,
+    in one vectorised call: ties go to the even code."""
+    t = _table(oracle_lib)
+    c = np.arange(0x7E)
+    mids = ((t[c] + t[c + 1]) / 2).astype(np.float32)
+    even = np.where(c % 2 == 0, c, c + 1).astype(np.uint8)
+    assert np.array_equal(oracle_lib.fp8_encode_array(mids), even)
+    assert np.array_equal(oracle_lib.fp8_encode_array(-mids), even | 0x80)
+
+
 def test_brute_force_nearest_code(oracle_lib):
     """Nearest code by scanning the whole table, ties to the even code."""
     t = _table(oracle_lib)

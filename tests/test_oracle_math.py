@@ -178,6 +178,34 @@ def test_layernorm_matches_torch_float64(oracle_lib):
     assert np.all(np.abs(y - ref) <= 2e-6 * scale)
 
 
+def test_bf16_writer_rounds_like_torch_bf16(oracle_lib):
+    """The bf16-intermediate writer at position 0 (identity rotation) returns
+    bf16(LayerNorm output); torch's float -> bfloat16 conversion (nearest,
+    ties to even) is the library reference."""
+    wl = W.named(1)
+    z = np.zeros(wl.T, np.int64)
+    n32, _ = oracle_lib.k_values(wl.k, wl.gamma, wl.beta, wl.eps, z, wl.cos, wl.sin)
+    n16, _ = oracle_lib.k_values(wl.k, wl.gamma, wl.beta, wl.eps, z, wl.cos, wl.sin, bf16_mode=1)
+    ref = torch.from_numpy(n32).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(bits(n16), bits(ref))
+
+
+def test_bf16_writer_ties_go_to_even(oracle_lib):
+    """A constant key row normalises to beta exactly, so beta set to exact bf16
+    midpoints makes the writer's first rounding a tie (position 0: identity
+    rotation, so the second rounding sees bf16 values and changes nothing).
+    Ties go to the even bf16 value, as torch rounds."""
+    k = W.f32_to_bf16_bits(np.full((1, ROW), 3.0, np.float32))
+    mids = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(2 + 2 ** -7), -(2 + 3 * 2 ** -7)], np.float32)
+    beta = np.resize(mids, ROW).astype(np.float32)
+    cos, sin = W.rope_table(2, 64)
+    y, _ = oracle_lib.k_values(k, np.ones(ROW, np.float32), beta, 1e-6, np.zeros(1, np.int64),
+                               cos, sin, bf16_mode=1)
+    want = np.resize(np.array([1.0, 1 + 2 ** -6, -2.0, -(2 + 2 ** -5)], np.float32), ROW)
+    assert np.array_equal(y[0], want)
+    assert np.array_equal(torch.from_numpy(beta).to(torch.bfloat16).to(torch.float32).numpy(), want)
+
+
 def test_layernorm_constant_row_gives_beta(oracle_lib):
     k = bf16(np.full((3, ROW), 2.5, np.float32))
     g = np.linspace(0.5, 1.5, ROW).astype(np.float32)
