@@ -281,6 +281,18 @@ def main():
                                          "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
         del sets
         torch.cuda.empty_cache()
+        # top-k per row over index logits (index_topk = 2048)
+        for ti in range(len(W.TOPK_NAMED)):
+            tw = W.topk_named(ti)
+            lg = torch.from_numpy(tw.logits).cuda()
+            ln = torch.from_numpy(tw.lengths).cuda()
+            ot = torch.empty((tw.logits.shape[0], tw.k), dtype=torch.int32, device="cuda")
+            mst = time_calls(torch, lambda: R.dsaidx_topk_per_row(lg, tw.k, ot, ln), 50, 5)
+            bt = W.topk_bytes_per_call(tw.logits.shape[0], tw.lengths, tw.k)
+            extras[tw.name] = {"us_per_call": mst * 1e3, "algorithmic_bytes": bt,
+                               "achieved_GBps": bt / (mst * 1e-3) / 1e9}
+            del lg, ln, ot
+        torch.cuda.empty_cache()
         result["secondary"] = extras
 
     # plain device copy of the same byte count: the reference for achievable

@@ -218,6 +218,26 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
 dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
                                           dsaidx_stream_t stream);
 
+/* Top-k per row: the selection that follows the index logits, each query
+ * keeping its index_topk highest-scoring keys ([sglang-fuse] Benchmark:
+ * index_topk = 2048; [vllm-47335] Kernel-level evidence: the top-k-per-row
+ * decode launch after the paged MQA logits).
+ *   logits     fp32 [rows, row_stride] (device), 16-byte aligned; the buffer holds
+ *              rows * row_stride floats; row r is valid over [0, len_r) with
+ *              len_r = min(max(lengths[r], 0), cols) (lengths NULL: len_r = cols)
+ *   row_stride floats between rows, >= cols and a multiple of 4
+ *   lengths    int32 [rows] (device) or NULL
+ *   rows       >= 0 and < 2^31;  cols in [0, 2^31);  k in [1, 2^20]
+ *   out_idx    out: int32 [rows, k] (device), 4-byte aligned.  When len_r > k: the
+ *              indices of the k largest valid logits, in no particular order; when
+ *              several logits equal the k-th largest, which of them are taken is
+ *              not specified (the multiset of selected values is).  When
+ *              len_r <= k: 0, 1, ..., len_r - 1, then -1.
+ * Logits must not be NaN.  One dispatch; no allocation. */
+dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                  int64_t rows, int64_t cols, int32_t k, int32_t* out_idx,
+                                  dsaidx_stream_t stream);
+
 /* Encode n fp32 values to E4M3FN bytes with the device conversion every
  * kernel above uses (round to nearest even), so the conversion can be checked
  * on its own against the format definition.  in: device fp32 [n], 4-byte

@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     dsaidx_q_rope_quant_fold,
     dsaidx_qk_fused,
     dsaidx_status_string,
+    dsaidx_topk_per_row,
     k_args,
     lib,
     q_args,

@@ -26,7 +26,8 @@ DSAIDX_K_PAGED_CACHE = 0x2
 PAGED_SLOT_BYTES = ROW + 4   # one code row and one fp32 scale per slot
 EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaidx_qk_fused",
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
-            "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest")
+            "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest",
+            "dsaidx_topk_per_row")
 
 
 class DsaidxError(RuntimeError):
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.dsaidx_topk_per_row.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int32, P, P]
+        L.dsaidx_topk_per_row.restype = ctypes.c_int
         L.dsaidx_fp8_encode_selftest.argtypes = [P, P, ctypes.c_int64, P]
         L.dsaidx_fp8_encode_selftest.restype = ctypes.c_int
         L.dsaidx_device_supported.argtypes = [ctypes.c_int]
@@ -164,6 +168,25 @@ def dsaidx_fp8_encode_selftest(inp, out, stream=None) -> None:
     _check(lib().dsaidx_fp8_encode_selftest(ctypes.c_void_p(_ptr(inp)), ctypes.c_void_p(_ptr(out)),
                                             inp.numel(), _stream_handle(stream)),
            "dsaidx_fp8_encode_selftest")
+
+
+def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None) -> None:
+    """logits: float32 device tensor [rows, cols] with unit column stride and a
+    row stride that is a multiple of 4; lengths: int32 [rows] or None; out:
+    contiguous int32 [rows, k]."""
+    import torch
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
+          "logits must be float32 [rows, cols] with unit column stride")
+    rows, cols = logits.shape
+    _need(out.dtype == torch.int32 and tuple(out.shape) == (rows, k) and out.is_contiguous(),
+          "out must be contiguous int32 [rows, k]")
+    if lengths is not None:
+        _need(lengths.dtype == torch.int32 and lengths.numel() == rows and lengths.is_contiguous(),
+              "lengths must be contiguous int32 [rows]")
+    _check(lib().dsaidx_topk_per_row(ctypes.c_void_p(_ptr(logits)), logits.stride(0) if rows else cols,
+                                     ctypes.c_void_p(_ptr(lengths)), rows, cols, int(k),
+                                     ctypes.c_void_p(_ptr(out)), _stream_handle(stream)),
+           "dsaidx_topk_per_row")
 
 
 # ------------------------------------------- struct builders from tensors ----

@@ -223,6 +223,21 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     return launch(p, rope->style, qb + kb, kBlock, stream);
 }
 
+dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                  int64_t rows, int64_t cols, int32_t k, int32_t* out_idx,
+                                  dsaidx_stream_t stream) {
+    if (rows < 0 || rows >= (int64_t(1) << 31) || cols < 0 || cols >= (int64_t(1) << 31) ||
+        k < 1 || k > (1 << 20))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return DSAIDX_OK;
+    if (!logits || !out_idx || !aligned(logits, 16) || !aligned(out_idx, 4) ||
+        (lengths && !aligned(lengths, 4)))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (row_stride < cols || row_stride % 4 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    return to_status(dsaidx::launch_topk(logits, row_stride, lengths, rows, cols, k, out_idx,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,
                                          dsaidx_stream_t stream) {
     if (n < 0 || !in || !out || !aligned(in, 4) || !aligned(out, 8))

@@ -65,6 +65,10 @@ struct PrepParams {
 hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned block,
                        hipStream_t stream);
 
+// Enqueue the top-k-per-row selection (one workgroup per row).
+hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* lengths,
+                       int64_t rows, int64_t cols, int32_t k, int32_t* out, hipStream_t stream);
+
 // Enqueue the stand-alone E4M3FN conversion (self-test of the device encoder).
 hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigned grid,
                                hipStream_t stream);

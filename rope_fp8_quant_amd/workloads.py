@@ -220,3 +220,55 @@ def bytes_per_call(T: int, H: int = 64, entry: str = "fused", rope_dim: int = 64
     once per call for the entries that run K rows."""
     per_call = 0 if entry == "q" else 2 * ROW * 4
     return T * bytes_per_token(H, entry, rope_dim) + per_call
+
+
+# ------------------------------------------------ top-k per row inputs ----
+
+@dataclass
+class TopkWorkload:
+    name: str
+    logits: np.ndarray      # float32 [rows, cols]
+    lengths: np.ndarray     # int32 [rows]: valid columns of each row
+    k: int
+
+
+def topk_make(rows: int, cols: int, k: int = 2048, *, lengths: str = "full", seed: int = 0,
+              name: str = "custom") -> TopkWorkload:
+    """Index logits for the top-k selection.  Values N(0,1) float32; every
+    fourth row rounded to multiples of 1/8 (many ties); 1% of the entries
+    -inf (masked keys).  lengths: "full" (every column), "ragged" (uniform in
+    [cols/2, cols]) or "causal" (row r of the last `rows` queries of a
+    `cols`-token context sees cols - rows + 1 + r keys)."""
+    kids = np.random.SeedSequence(seed).spawn(3)
+    rv, rm, rl = (np.random.default_rng(s) for s in kids)
+    x = rv.standard_normal((rows, cols), dtype=np.float32)
+    x[::4] = np.round(x[::4] * 8) / 8
+    mask = rm.random((rows, cols)) < 0.01
+    x[mask] = -np.inf
+    if lengths == "full":
+        lens = np.full(rows, cols, np.int32)
+    elif lengths == "ragged":
+        lens = rl.integers(cols // 2, cols + 1, rows).astype(np.int32)
+    elif lengths == "causal":
+        lens = (cols - rows + 1 + np.arange(rows)).astype(np.int32)
+    else:
+        raise ValueError(lengths)
+    return TopkWorkload(name=name, logits=x, lengths=lens, k=k)
+
+
+TOPK_NAMED = [
+    ("topk_decode_batch64_ctx16384", dict(rows=64, cols=16384, lengths="ragged")),
+    ("topk_decode_batch64_ctx131072", dict(rows=64, cols=131072, lengths="ragged")),
+    ("topk_prefill_causal_T8192", dict(rows=8192, cols=8192, lengths="causal")),
+]
+
+
+def topk_named(idx: int) -> TopkWorkload:
+    name, kw = TOPK_NAMED[idx]
+    return topk_make(seed=2000 + idx, name=name, **kw)
+
+
+def topk_bytes_per_call(rows: int, lengths, k: int = 2048) -> int:
+    """Algorithmic bytes: every valid logit read once, the length of each row,
+    and k indices written per row."""
+    return int(np.sum(np.asarray(lengths, dtype=np.int64))) * 4 + rows * 4 + rows * k * 4

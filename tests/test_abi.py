@@ -193,3 +193,20 @@ def test_fp8_selftest_argument_checks(L):
     assert L.dsaidx_fp8_encode_selftest(FAKE, None, 8, None) == 1
     assert L.dsaidx_fp8_encode_selftest(FAKE + 2, FAKE, 8, None) == 1
     assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE + 4, 8, None) == 1
+
+
+def test_topk_argument_checks(L):
+    P = ctypes.c_void_p
+    ok = dict(logits=FAKE, row_stride=2048, lengths=None, rows=4, cols=2048, k=64, out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.dsaidx_topk_per_row(P(a["logits"]), a["row_stride"], P(a["lengths"]), a["rows"],
+                                     a["cols"], a["k"], P(a["out"]), None)
+    assert call(rows=0) == B.DSAIDX_OK
+    assert call(rows=0, logits=None, out=None) == B.DSAIDX_OK
+    for bad in (dict(rows=-1), dict(rows=1 << 31), dict(cols=-1), dict(cols=1 << 31), dict(k=0),
+                dict(k=(1 << 20) + 1), dict(logits=None), dict(out=None), dict(logits=FAKE + 4),
+                dict(out=FAKE + 2), dict(lengths=FAKE + 2), dict(row_stride=2047),
+                dict(row_stride=2050), dict(row_stride=1024)):
+        assert call(**bad) == B.DSAIDX_ERR_INVALID_ARGUMENT, bad

@@ -1,0 +1,135 @@
+"""GPU parity of dsaidx_topk_per_row against the top-k oracle.
+
+Acceptance: where a row has more than k valid logits, the k returned indices
+are distinct, valid (inside the row's length) and select exactly the oracle's
+multiset of the k largest values (ties at the k-th place may be broken either
+way); where it has at most k, the result is 0..len-1 followed by -1.
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import rope_fp8_quant_amd as R
+from oracle import topk as TK
+from rope_fp8_quant_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def run_topk(logits: np.ndarray, k: int, lengths=None, pad_cols: int = 0, pad_value=np.inf):
+    rows, cols = logits.shape
+    stride = cols + pad_cols
+    stride += (-stride) % 4
+    buf = np.full((rows, stride), pad_value, np.float32)
+    buf[:, :cols] = logits
+    d = torch.from_numpy(buf).cuda()[:, :cols]
+    dl = None if lengths is None else torch.from_numpy(np.asarray(lengths, np.int32)).cuda()
+    out = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    R.dsaidx_topk_per_row(d, k, out, dl)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(idx: np.ndarray, logits: np.ndarray, k: int, lengths=None):
+    rows, cols = logits.shape
+    lens = TK.row_lengths(rows, cols, lengths)
+    want_vals, count = TK.topk_values(logits, k, lengths)
+    ties_broken = 0
+    for r in range(rows):
+        n = int(lens[r])
+        if n <= k:
+            assert np.array_equal(idx[r], np.concatenate([np.arange(n), np.full(k - n, -1)])), r
+            continue
+        sel = idx[r]
+        assert np.all((sel >= 0) & (sel < n)), r
+        assert np.unique(sel).size == k, r
+        got = np.sort(logits[r, sel])[::-1]
+        assert np.array_equal(got, want_vals[r]), r       # -0 == +0 compares equal
+        kth = want_vals[r, k - 1]
+        ties_broken += int(np.count_nonzero(logits[r, :n] == kth) > np.count_nonzero(got == kth))
+    return ties_broken
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_named_workloads(idx):
+    wl = W.topk_named(idx)
+    out = run_topk(wl.logits, wl.k, wl.lengths)
+    tb = check(out, wl.logits, wl.k, wl.lengths)
+    print("\n[parity] topk %s %s" % (wl.name, json.dumps(dict(rows=int(wl.logits.shape[0]),
+                                                               rows_with_tied_kth=tb))), flush=True)
+
+
+@pytest.mark.parametrize("k", [1, 2, 7, 255, 2048, 4095])
+def test_k_values(k):
+    wl = W.topk_make(19, 4099, k=k, lengths="ragged", seed=k)
+    out = run_topk(wl.logits, k, wl.lengths, pad_cols=5)
+    check(out, wl.logits, k, wl.lengths)
+
+
+def test_all_equal_rows_and_special_values():
+    rows, cols, k = 6, 1000, 100
+    x = np.zeros((rows, cols), np.float32)
+    x[1] = 3.5                                   # every value ties
+    x[2, ::2] = -0.0                             # +0 and -0 (equal values)
+    x[3] = -np.inf
+    x[3, 17] = 1.0
+    x[4] = np.linspace(-1, 1, cols, dtype=np.float32)
+    x[4, 900:] = np.inf
+    x[5] = np.float32(1e-42)                     # fp32 subnormals
+    x[5, 5] = np.float32(2e-42)
+    out = run_topk(x, k)
+    check(out, x, k)
+    assert 17 in out[3]
+    assert set(range(900, 1000)) == set(out[4].tolist())
+
+
+def test_lengths_edge_cases():
+    rng = np.random.default_rng(3)
+    rows, cols, k = 8, 3000, 256
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    lens = np.array([0, 1, 255, 256, 257, 3000, 5000, -3], np.int32)
+    out = run_topk(x, k, lens, pad_cols=11, pad_value=np.inf)
+    check(out, x, k, lens)
+    out = run_topk(x, k, None, pad_cols=11, pad_value=np.inf)
+    check(out, x, k, None)
+
+
+def test_many_rows_prefill_shape():
+    wl = W.topk_make(3000, 4096, k=512, lengths="causal", seed=8)
+    out = run_topk(wl.logits, 512, wl.lengths)
+    check(out, wl.logits, 512, wl.lengths)
+
+
+def test_empty_and_invalid_calls():
+    x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    out = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    R.dsaidx_topk_per_row(x, 8, out)
+    x = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    out = torch.zeros((4, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(R.DsaidxError):
+        R.dsaidx_topk_per_row(x[:, 1:], 8, out)   # data pointer not 16-byte aligned
+
+
+def test_degenerate_value_ranges():
+    """Spans that defeat the linear coarse binning (huge, subnormal, a single
+    finite value among infinities) fall back to the exact selection."""
+    rows, cols, k = 5, 6000, 300
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[0, :3] = [-3e38, 3e38, 1e38]                         # span overflows fp32
+    x[1] = np.float32(1e-44) * rng.integers(0, 5, cols).astype(np.float32)   # subnormal span
+    x[2] = -np.inf
+    x[2, 100:500] = 2.0                                    # one finite value
+    x[3] = np.round(x[3])                                  # few distinct values: heavy ties
+    x[4, :] = 7.0
+    x[4, 4000:4300] = np.inf
+    out = run_topk(x, k)
+    check(out, x, k)
