@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DSAIDX_ABI_VERSION 2
+#define DSAIDX_ABI_VERSION 3
 #define DSAIDX_HEAD_DIM 128 /* width of every head vector and K row */
 
 typedef struct ihipStream_t* dsaidx_stream_t; /* the same type as hipStream_t */
@@ -233,10 +233,24 @@ dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_r
  *              several logits equal the k-th largest, which of them are taken is
  *              not specified (the multiset of selected values is).  When
  *              len_r <= k: 0, 1, ..., len_r - 1, then -1.
- * Logits must not be NaN.  One dispatch; no allocation. */
+ *   workspace  device scratch of at least dsaidx_topk_workspace_bytes(rows, cols, k)
+ *              bytes, 16-byte aligned, owned by the caller; its contents on entry
+ *              do not matter and are overwritten.  May be NULL when that size is 0.
+ *   workspace_bytes  its size.
+ * Logits must not be NaN.  One dispatch, or two for rows longer than 32768
+ * logits (per-chunk selection into the workspace, then a merge); no
+ * allocation.  Calls that share a workspace must be ordered on one stream.
+ * A workspace that is required but NULL, misaligned or too small is
+ * DSAIDX_ERR_INVALID_ARGUMENT. */
 dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const int32_t* lengths,
                                   int64_t rows, int64_t cols, int32_t k, int32_t* out_idx,
+                                  void* workspace, int64_t workspace_bytes,
                                   dsaidx_stream_t stream);
+
+/* Bytes of workspace dsaidx_topk_per_row needs for this shape: 0 for rows of
+ * at most 32768 logits, rows * chunks * k * 8 (chunks of 16384 logits) when the
+ * two-dispatch path runs; -1 for a shape dsaidx_topk_per_row rejects. */
+int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
 
 /* Encode n fp32 values to E4M3FN bytes with the device conversion every
  * kernel above uses (round to nearest even), so the conversion can be checked

@@ -27,7 +27,7 @@ PAGED_SLOT_BYTES = ROW + 4   # one code row and one fp32 scale per slot
 EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaidx_qk_fused",
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
             "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest",
-            "dsaidx_topk_per_row")
+            "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes")
 
 
 class DsaidxError(RuntimeError):
@@ -86,8 +86,10 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.dsaidx_topk_per_row.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64,
-                                          ctypes.c_int32, P, P]
+                                          ctypes.c_int32, P, P, ctypes.c_int64, P]
         L.dsaidx_topk_per_row.restype = ctypes.c_int
+        L.dsaidx_topk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+        L.dsaidx_topk_workspace_bytes.restype = ctypes.c_int64
         L.dsaidx_fp8_encode_selftest.argtypes = [P, P, ctypes.c_int64, P]
         L.dsaidx_fp8_encode_selftest.restype = ctypes.c_int
         L.dsaidx_device_supported.argtypes = [ctypes.c_int]
@@ -170,10 +172,21 @@ def dsaidx_fp8_encode_selftest(inp, out, stream=None) -> None:
            "dsaidx_fp8_encode_selftest")
 
 
-def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None) -> None:
+def dsaidx_topk_workspace_bytes(rows: int, cols: int, k: int) -> int:
+    """Workspace bytes dsaidx_topk_per_row needs for this shape (0 for most)."""
+    n = lib().dsaidx_topk_workspace_bytes(int(rows), int(cols), int(k))
+    if n < 0:
+        raise DsaidxError(DSAIDX_ERR_INVALID_ARGUMENT, "dsaidx_topk_workspace_bytes")
+    return n
+
+
+def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None, workspace=None) -> None:
     """logits: float32 device tensor [rows, cols] with unit column stride and a
     row stride that is a multiple of 4; lengths: int32 [rows] or None; out:
-    contiguous int32 [rows, k]."""
+    contiguous int32 [rows, k]; workspace: a contiguous device tensor of at
+    least dsaidx_topk_workspace_bytes(rows, cols, k) bytes, or None to have one
+    allocated here when that size is not 0 (keep one to reuse, e.g. under graph
+    capture)."""
     import torch
     _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
           "logits must be float32 [rows, cols] with unit column stride")
@@ -183,9 +196,18 @@ def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None) -> None:
     if lengths is not None:
         _need(lengths.dtype == torch.int32 and lengths.numel() == rows and lengths.is_contiguous(),
               "lengths must be contiguous int32 [rows]")
+    ws_bytes = 0
+    if workspace is None:
+        need = dsaidx_topk_workspace_bytes(rows, cols, k)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    if workspace is not None:
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().dsaidx_topk_per_row(ctypes.c_void_p(_ptr(logits)), logits.stride(0) if rows else cols,
                                      ctypes.c_void_p(_ptr(lengths)), rows, cols, int(k),
-                                     ctypes.c_void_p(_ptr(out)), _stream_handle(stream)),
+                                     ctypes.c_void_p(_ptr(out)), ctypes.c_void_p(_ptr(workspace)),
+                                     ws_bytes, _stream_handle(stream)),
            "dsaidx_topk_per_row")
 
 

@@ -223,19 +223,31 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     return launch(p, rope->style, qb + kb, kBlock, stream);
 }
 
+static bool topk_shape_ok(int64_t rows, int64_t cols, int32_t k) {
+    return rows >= 0 && rows < (int64_t(1) << 31) && cols >= 0 && cols < (int64_t(1) << 31) &&
+           k >= 1 && k <= (1 << 20);
+}
+
+int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k) {
+    if (!topk_shape_ok(rows, cols, k)) return -1;
+    return dsaidx::topk_workspace_bytes(rows, cols, k);
+}
+
 dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const int32_t* lengths,
                                   int64_t rows, int64_t cols, int32_t k, int32_t* out_idx,
+                                  void* workspace, int64_t workspace_bytes,
                                   dsaidx_stream_t stream) {
-    if (rows < 0 || rows >= (int64_t(1) << 31) || cols < 0 || cols >= (int64_t(1) << 31) ||
-        k < 1 || k > (1 << 20))
-        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!topk_shape_ok(rows, cols, k)) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (rows == 0) return DSAIDX_OK;
     if (!logits || !out_idx || !aligned(logits, 16) || !aligned(out_idx, 4) ||
         (lengths && !aligned(lengths, 4)))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (row_stride < cols || row_stride % 4 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    const int64_t need = dsaidx::topk_workspace_bytes(rows, cols, k);
+    if (need > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < need))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
     return to_status(dsaidx::launch_topk(logits, row_stride, lengths, rows, cols, k, out_idx,
-                                         reinterpret_cast<hipStream_t>(stream)));
+                                         workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,

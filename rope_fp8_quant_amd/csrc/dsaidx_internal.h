@@ -65,9 +65,14 @@ struct PrepParams {
 hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned block,
                        hipStream_t stream);
 
-// Enqueue the top-k-per-row selection (one workgroup per row).
+// Workspace bytes the top-k selection needs for this shape (0 for most).
+int64_t topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
+
+// Enqueue the top-k-per-row selection (one or two dispatches); `workspace`
+// holds topk_workspace_bytes(rows, cols, k) bytes.
 hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* lengths,
-                       int64_t rows, int64_t cols, int32_t k, int32_t* out, hipStream_t stream);
+                       int64_t rows, int64_t cols, int32_t k, int32_t* out, void* workspace,
+                       hipStream_t stream);
 
 // Enqueue the stand-alone E4M3FN conversion (self-test of the device encoder).
 hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigned grid,

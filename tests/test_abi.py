@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_struct_sizes(L):
-    assert B.dsaidx_abi_version() == 2
+    assert B.dsaidx_abi_version() == 3
     assert L.dsaidx_struct_size(0) == ctypes.sizeof(B.DsaidxRope) == 40
     assert L.dsaidx_struct_size(1) == ctypes.sizeof(B.DsaidxQArgs) == 88
     assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 104
@@ -202,7 +202,8 @@ def test_topk_argument_checks(L):
     def call(**kw):
         a = dict(ok, **kw)
         return L.dsaidx_topk_per_row(P(a["logits"]), a["row_stride"], P(a["lengths"]), a["rows"],
-                                     a["cols"], a["k"], P(a["out"]), None)
+                                     a["cols"], a["k"], P(a["out"]), P(a.get("ws")),
+                                     a.get("ws_bytes", 0), None)
     assert call(rows=0) == B.DSAIDX_OK
     assert call(rows=0, logits=None, out=None) == B.DSAIDX_OK
     for bad in (dict(rows=-1), dict(rows=1 << 31), dict(cols=-1), dict(cols=1 << 31), dict(k=0),
@@ -210,3 +211,24 @@ def test_topk_argument_checks(L):
                 dict(out=FAKE + 2), dict(lengths=FAKE + 2), dict(row_stride=2047),
                 dict(row_stride=2050), dict(row_stride=1024)):
         assert call(**bad) == B.DSAIDX_ERR_INVALID_ARGUMENT, bad
+
+
+def test_topk_workspace_size_and_checks(L):
+    P = ctypes.c_void_p
+    ws = L.dsaidx_topk_workspace_bytes
+    assert ws(64, 16384, 2048) == 0
+    assert ws(64, 32768, 2048) == 0
+    assert ws(64, 131072, 2048) == 64 * 8 * 2048 * 8
+    assert ws(3, 32769, 7) == 3 * 3 * 7 * 8
+    assert ws(64, 50000, 12000) == 0          # k too large for the chunked path
+    assert ws(0, 131072, 2048) == 0
+    assert ws(-1, 10, 1) == -1 and ws(1, 10, 0) == -1 and ws(1, -1, 1) == -1
+    need = ws(2, 131072, 2048)
+
+    def call(w, nbytes, rows=2, cols=131072):
+        return L.dsaidx_topk_per_row(P(FAKE), cols, None, rows, cols, 2048, P(FAKE), P(w), nbytes,
+                                     None)
+    assert call(None, 0) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call(FAKE, need - 1) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call(FAKE + 4, need) == B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call(None, 0, rows=0) == B.DSAIDX_OK

@@ -133,3 +133,54 @@ def test_degenerate_value_ranges():
     x[4, 4000:4300] = np.inf
     out = run_topk(x, k)
     check(out, x, k)
+
+
+# Every launch variant: register-resident rows of up to 4096 / 8192 / 16384 /
+# 32768 logits, the two-dispatch chunk + merge path (merge of up to 16384 and
+# up to 32768 candidates), and the generic kernel for k too large for those.
+@pytest.mark.parametrize("rows,cols,k,lengths,ws", [
+    (5, 4096, 2048, "full", 0),
+    (5, 8000, 2048, "ragged", 0),
+    (5, 16384, 2048, "full", 0),
+    (6, 30001, 2048, "ragged", 0),
+    (6, 32768, 10000, "full", 0),
+    (9, 131072, 2048, "ragged", 1),
+    (4, 200000, 2048, "ragged", 1),
+    (4, 65536, 1003, "full", 1),
+    (3, 40000, 7, "ragged", 1),
+    (3, 50000, 12000, "full", 0),
+    (2, 40000, 20000, "ragged", 0),
+])
+def test_launch_variants(rows, cols, k, lengths, ws):
+    wl = W.topk_make(rows, cols, k=k, lengths=lengths, seed=cols + k)
+    assert (R.dsaidx_topk_workspace_bytes(rows, cols, k) > 0) == bool(ws)
+    out = run_topk(wl.logits, k, wl.lengths)
+    check(out, wl.logits, k, wl.lengths)
+
+
+def test_two_phase_row_lengths():
+    """Rows of the chunk + merge path that end inside the first chunk, exactly at
+    a chunk edge, a few logits into a chunk, and rows of at most k logits."""
+    rows, cols, k = 10, 70000, 2048
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    lens = np.array([0, 5, 2048, 2049, 16383, 16384, 16385, 32768 + 3, 69999, 70000], np.int32)
+    out = run_topk(x, k, lens)
+    check(out, x, k, lens)
+
+
+def test_workspace_reuse_and_too_small():
+    rows, cols, k = 4, 100000, 2048
+    wl = W.topk_make(rows, cols, k=k, lengths="ragged", seed=5)
+    need = R.dsaidx_topk_workspace_bytes(rows, cols, k)
+    assert need == rows * 7 * k * 8
+    d = torch.from_numpy(wl.logits).cuda()
+    dl = torch.from_numpy(wl.lengths).cuda()
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    out = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        R.dsaidx_topk_per_row(d, k, out, dl, workspace=ws)
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), wl.logits, k, wl.lengths)
+    with pytest.raises(R.DsaidxError):
+        R.dsaidx_topk_per_row(d, k, out, dl, workspace=ws[: need - 16])
