@@ -237,19 +237,21 @@ dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_r
  *              bytes, 16-byte aligned, owned by the caller; its contents on entry
  *              do not matter and are overwritten.  May be NULL when that size is 0.
  *   workspace_bytes  its size.
- * Logits must not be NaN.  One dispatch, or two for rows longer than 32768
- * logits (per-chunk selection into the workspace, then a merge); no
- * allocation.  Calls that share a workspace must be ordered on one stream.
- * A workspace that is required but NULL, misaligned or too small is
- * DSAIDX_ERR_INVALID_ARGUMENT. */
+ * Logits must not be NaN.  One dispatch for rows of up to 32768 logits; four
+ * for longer rows (the row spread over workgroups of 4096 logits, with the row's
+ * histograms, counters and candidate list in the workspace); no allocation.
+ * Calls that share a workspace must be ordered on one stream.  A workspace that
+ * is required but NULL, misaligned or too small is DSAIDX_ERR_INVALID_ARGUMENT. */
 dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const int32_t* lengths,
                                   int64_t rows, int64_t cols, int32_t k, int32_t* out_idx,
                                   void* workspace, int64_t workspace_bytes,
                                   dsaidx_stream_t stream);
 
-/* Bytes of workspace dsaidx_topk_per_row needs for this shape: 0 for rows of
- * at most 32768 logits, rows * chunks * k * 8 (chunks of 16384 logits) when the
- * two-dispatch path runs; -1 for a shape dsaidx_topk_per_row rejects. */
+/* Bytes of workspace dsaidx_topk_per_row needs for this shape: 0 when
+ * cols <= 32768, else rows * (16416 + 8 * cols rounded up to a multiple of 4)
+ * (per row: two 2048-bin histograms and counters, and a list of up to cols
+ * candidate keys and indices); -1 for a shape dsaidx_topk_per_row rejects
+ * (including rows * ceil(cols / 4096) >= 2^31 when cols > 32768). */
 int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
 
 /* Encode n fp32 values to E4M3FN bytes with the device conversion every

@@ -244,6 +244,7 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (row_stride < cols || row_stride % 4 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
     const int64_t need = dsaidx::topk_workspace_bytes(rows, cols, k);
+    if (need < 0) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (need > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < need))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     return to_status(dsaidx::launch_topk(logits, row_stride, lengths, rows, cols, k, out_idx,

@@ -65,10 +65,11 @@ struct PrepParams {
 hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned block,
                        hipStream_t stream);
 
-// Workspace bytes the top-k selection needs for this shape (0 for most).
+// Workspace bytes the top-k selection needs for this shape: 0 for rows of up
+// to 32768 logits, -1 for a shape too large to launch.
 int64_t topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
 
-// Enqueue the top-k-per-row selection (one or two dispatches); `workspace`
+// Enqueue the top-k-per-row selection (one or four dispatches); `workspace`
 // holds topk_workspace_bytes(rows, cols, k) bytes.
 hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* lengths,
                        int64_t rows, int64_t cols, int32_t k, int32_t* out, void* workspace,

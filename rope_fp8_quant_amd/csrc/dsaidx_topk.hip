@@ -5,39 +5,33 @@
 // MQA logits, vLLM PR 47335 "Enable fused indexer-Q RoPE+quant kernel", section
 // Kernel-level evidence).
 //
-// Register-resident selection (topk_reg_kernel): one workgroup per segment of
-// at most T*V logits, each thread holding V of them in registers for the whole
-// selection, so the row is read from HBM exactly once and LDS holds only two
-// 2048-bin histograms:
-//   1. min and max of the finite logits (workgroup reduction);
-//   2. a 2048-bin histogram of a coarse bin index that is a monotone function
-//      of the value (linear between min and max, -inf first, +inf last): the
-//      spread keeps the LDS atomics nearly conflict-free.  A scan from the top
-//      finds the bin B1 holding the k-th largest logit and its rank in B1;
-//   3. an exact radix select inside B1 on order-preserving 32-bit keys (the
-//      float bits with the sign flipped for positives, all bits flipped for
-//      negatives), taken relative to the smallest key in B1 so that only the
-//      bits that differ are examined: digits of up to 11 bits, most often two
-//      passes, none when B1 holds one distinct value;
-//   4. with the k-th largest key K known, the logits above K and the first
-//      needed ones equal to K are written to slots given by one workgroup
-//      prefix sum (no atomics, deterministic).
-// Segments are whole rows (rows up to 32768 logits), or, for longer rows, two
-// launches: chunks of 16384 logits each keep their own top-k (values and
-// indices into a caller workspace), then one workgroup per row selects the
-// top-k of those candidates.
+// Both paths select on order-preserving 32-bit keys: the float bits with the
+// sign flipped for positives and all bits flipped for negatives, so unsigned
+// key order is value order (-0 just below +0; NaN is outside the contract).
 //
-// Rows and k outside those shapes take topk_generic_kernel: one 1024-thread
-// workgroup per row that streams the row (from LDS when it fits) through the
-// same coarse histogram, compacts B1 into LDS, and radix-selects there (or over
-// the row when B1 does not fit).
+// Rows of up to 32768 logits (topk_row_kernel): one workgroup per row, each
+// thread holding V of the row's logits in registers for the whole selection,
+// so the row is read from HBM once and LDS holds only two 2048-bin histograms
+// and a short list:
+//   1. min and max of the finite keys (workgroup reduction);
+//   2. a 2048-bin histogram of a coarse bin index that is a monotone function
+//      of the value (linear between min and max): the spread keeps the LDS
+//      atomics nearly conflict-free.  A scan from the top finds the bin B1
+//      holding the k-th largest logit and its rank in B1;
+//   3. logits in bins above B1 are written at slots given by one workgroup
+//      prefix sum (no atomics); B1's logits go to an LDS list;
+//   4. a list of at most 64 is ranked by one wavefront directly; a longer one
+//      is radix-selected on keys relative to its smallest key (11-bit digits,
+//      most often two passes, none for a tie group), over the list or, when
+//      B1 overflows it, over the registers; then the list's keys above the
+//      k-th and the needed keys equal to it fill the remaining slots.
+// Longer rows take the split-row path below (four dispatches over a caller
+// workspace), which spreads one row over many workgroups.
 #include "dsaidx_internal.h"
 
 namespace dsaidx {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -49,252 +43,6 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 __device__ __forceinline__ float key_value(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
-
-// Inclusive prefix sum over the 1024 threads of the workgroup (thread order).
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wave_totals) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
-    if (lane == 63) wave_totals[wave] = v;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wave_totals[w];
-    __syncthreads();
-    return v + before;
-}
-
-struct Shared {
-    uint32_t hist[kBins];
-    uint32_t wave_totals[kWaves];
-    float wave_min[kWaves], wave_max[kWaves];
-    uint32_t sel_prefix, sel_remaining, cnt_out, cnt_eq, cnt_cand;
-    float lo, scale;
-};
-
-// Slot for this lane among the lanes of its wavefront with pred set, taken
-// from *counter with one atomic per wavefront.  Every active lane calls it.
-__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
-    const unsigned long long mask = __ballot(pred);
-    if (mask == 0) return 0;
-    const int leader = __ffsll((long long)mask) - 1;
-    uint32_t base = 0;
-    if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = __shfl(base, leader, 64);
-    const uint32_t rank =
-        __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-    return base + rank;
-}
-
-// After a histogram of nbins bins (keys matching `prefix` only), pick the bin
-// holding the key of rank `remaining` from the top; every thread returns the
-// prefix extended by that bin (<< shift) and the rank inside it.
-__device__ __forceinline__ void pick_bin(Shared& sh, int nbins, int shift, uint32_t& prefix,
-                                         uint32_t& remaining) {
-    const int tid = threadIdx.x;
-    const int bhi = nbins - 1 - 2 * tid;  // thread t owns bins bhi, bhi - 1 (descending)
-    const int blo = bhi - 1;
-    const uint32_t chi = bhi >= 0 ? sh.hist[bhi] : 0u;
-    const uint32_t clo = blo >= 0 ? sh.hist[blo] : 0u;
-    const uint32_t incl = block_inclusive_scan(chi + clo, sh.wave_totals);
-    const uint32_t excl = incl - chi - clo;
-    if (excl < remaining && remaining <= incl) {
-        if (excl + chi >= remaining) {
-            sh.sel_prefix = prefix | ((uint32_t)bhi << shift);
-            sh.sel_remaining = remaining - excl;
-        } else {
-            sh.sel_prefix = prefix | ((uint32_t)blo << shift);
-            sh.sel_remaining = remaining - excl - chi;
-        }
-    }
-    __syncthreads();
-    prefix = sh.sel_prefix;
-    remaining = sh.sel_remaining;
-    __syncthreads();
-}
-
-__device__ __forceinline__ void clear_hist(Shared& sh, int nbins) {
-    for (int b = threadIdx.x; b < nbins; b += kThreads) sh.hist[b] = 0;
-    __syncthreads();
-}
-
-// Calls f(valid, index, value) for every element slot of the row, 16 bytes at
-// a time; all lanes of a wavefront call f together (valid may be false).
-template <typename F>
-__device__ __forceinline__ void for_each_value(const float4* src, int64_t len, F f) {
-    const int64_t chunks = (len + 3) >> 2;
-    const int64_t rounds = (chunks + kThreads - 1) / kThreads;
-    for (int64_t rd = 0; rd < rounds; ++rd) {
-        const int64_t c = rd * kThreads + threadIdx.x;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < chunks) v = src[c];
-        const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) f(c < chunks && 4 * c + m < len, 4 * c + m, e[m]);
-    }
-}
-
-// Coarse bin of a value: monotone non-decreasing in the value.
-__device__ __forceinline__ uint32_t coarse_bin(float v, float lo, float scale) {
-    if (v == -INFINITY) return 0;
-    if (v == INFINITY) return kBins - 1;
-    const float t = (v - lo) * scale;
-    const int b = (int)t;
-    return b < 0 ? 0u : (b > kBins - 1 ? (uint32_t)(kBins - 1) : (uint32_t)b);
-}
-
-template <int CACHE_FLOATS, int CAND>
-__global__ __launch_bounds__(kThreads) void topk_generic_kernel(const float* logits,
-                                                                int64_t row_stride,
-                                                                const int32_t* lengths,
-                                                                int64_t cols, int32_t k,
-                                                                int32_t* out) {
-    __shared__ Shared sh;
-    __shared__ uint32_t cand_key[CAND];
-    __shared__ int32_t cand_idx[CAND];
-    __shared__ float4 row_cache[CACHE_FLOATS > 0 ? CACHE_FLOATS / 4 : 1];
-
-    const int tid = threadIdx.x;
-    const int64_t r = blockIdx.x;
-    int32_t* dst = out + r * (int64_t)k;
-    int64_t len = cols;
-    if (lengths) {
-        const int64_t l = lengths[r];
-        len = l < 0 ? 0 : (l < cols ? l : cols);
-    }
-    if (len <= k) {
-        for (int64_t i = tid; i < k; i += kThreads) dst[i] = i < len ? (int32_t)i : -1;
-        return;
-    }
-    const float4* src = reinterpret_cast<const float4*>(logits + r * row_stride);
-    if (CACHE_FLOATS > 0) {
-        const int64_t chunks = (len + 3) >> 2;
-        for (int64_t c = tid; c < chunks; c += kThreads) row_cache[c] = src[c];
-        src = row_cache;
-    }
-
-    // 0. finite min and max
-    float mn = INFINITY, mx = -INFINITY;
-    for_each_value(src, len, [&](bool ok, int64_t, float v) {
-        if (ok && v > -INFINITY && v < INFINITY) {
-            mn = fminf(mn, v);
-            mx = fmaxf(mx, v);
-        }
-    });
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, d, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, d, 64));
-    }
-    if ((tid & 63) == 0) {
-        sh.wave_min[tid >> 6] = mn;
-        sh.wave_max[tid >> 6] = mx;
-    }
-    if (tid == 0) {
-        sh.cnt_out = 0;
-        sh.cnt_eq = 0;
-        sh.cnt_cand = 0;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float a = INFINITY, b = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) {
-            a = fminf(a, sh.wave_min[w]);
-            b = fmaxf(b, sh.wave_max[w]);
-        }
-        // A finite scale keeps (v - lo) * scale in [0, 2048] for every finite v;
-        // otherwise (one distinct finite value, or a span too small or too
-        // large for fp32) all finite values share one bin.
-        const float span = b - a;
-        const float sc = (a < b && span < INFINITY) ? (float)kBins / span : 0.0f;
-        sh.lo = a;
-        sh.scale = sc < INFINITY ? sc : 0.0f;
-    }
-    clear_hist(sh, kBins);
-    const float lo = sh.lo, scale = sh.scale;
-
-    // 1. coarse histogram, bin B1 of the k-th largest
-    for_each_value(src, len, [&](bool ok, int64_t, float v) {
-        if (ok) atomicAdd(&sh.hist[coarse_bin(v, lo, scale)], 1u);
-    });
-    __syncthreads();
-    uint32_t b1 = 0, rem = (uint32_t)k;
-    pick_bin(sh, kBins, 0, b1, rem);
-
-    // 2. bins above B1 go out; B1 becomes the candidates
-    for_each_value(src, len, [&](bool ok, int64_t i, float v) {
-        const uint32_t b = ok ? coarse_bin(v, lo, scale) : 0u;
-        const bool take = ok && b > b1;
-        const bool cand = ok && b == b1;
-        const uint32_t o = wave_append(&sh.cnt_out, take);
-        if (take) dst[o] = (int32_t)i;
-        const uint32_t c = wave_append(&sh.cnt_cand, cand);
-        if (cand && c < (uint32_t)CAND) {
-            cand_key[c] = order_key(v);
-            cand_idx[c] = (int32_t)i;
-        }
-    });
-    __syncthreads();
-    const uint32_t ncand = sh.cnt_cand;
-    const bool compact = ncand <= (uint32_t)CAND;
-
-    // 3. exact radix select of rank `rem` among the B1 logits
-    uint32_t prefix = 0;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int bits = pass < 2 ? 11 : 10;
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nbins = 1 << bits;
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + bits));
-        clear_hist(sh, nbins);
-        if (compact) {
-            for (uint32_t c = tid; c < ncand; c += kThreads) {
-                const uint32_t key = cand_key[c];
-                if ((key & hi_mask) == prefix)
-                    atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
-            }
-        } else {
-            for_each_value(src, len, [&](bool ok, int64_t, float v) {
-                const uint32_t key = order_key(v);
-                if (ok && coarse_bin(v, lo, scale) == b1 && (key & hi_mask) == prefix)
-                    atomicAdd(&sh.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
-            });
-        }
-        __syncthreads();
-        pick_bin(sh, nbins, shift, prefix, rem);
-    }
-
-    // prefix is the k-th largest key: the B1 keys above it go out, then `rem`
-    // keys equal to it fill [k - rem, k).
-    const uint32_t above = (uint32_t)k - rem;
-    if (compact) {
-        const uint32_t rounds = (ncand + kThreads - 1) / kThreads;
-        for (uint32_t rd = 0; rd < rounds; ++rd) {
-            const uint32_t c = rd * kThreads + tid;
-            const bool ok = c < ncand;
-            const uint32_t key = ok ? cand_key[c] : 0u;
-            const bool gt = ok && key > prefix, eq = ok && key == prefix;
-            const uint32_t o = wave_append(&sh.cnt_out, gt);
-            if (gt) dst[o] = cand_idx[c];
-            const uint32_t q = wave_append(&sh.cnt_eq, eq);
-            if (eq && q < rem) dst[above + q] = cand_idx[c];
-        }
-    } else {
-        for_each_value(src, len, [&](bool ok, int64_t i, float v) {
-            const uint32_t key = order_key(v);
-            const bool in_b1 = ok && coarse_bin(v, lo, scale) == b1;
-            const bool gt = in_b1 && key > prefix, eq = in_b1 && key == prefix;
-            const uint32_t o = wave_append(&sh.cnt_out, gt);
-            if (gt) dst[o] = (int32_t)i;
-            const uint32_t q = wave_append(&sh.cnt_eq, eq);
-            if (eq && q < rem) dst[above + q] = (int32_t)i;
-        });
-    }
-}
-
 
 // ------------------------------------------------ register-resident path ----
 
@@ -359,23 +107,21 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* pa
     return incl + before;
 }
 
-// Bins of `hist` are ranked from the top (bin kBins-1 first).  Finds the bin
-// holding the element of rank `want` (1-based, from the top) and the rank of
-// that element inside its bin; every thread returns both.  Thread t owns the
-// kBins/T bins just below kBins - t*kBins/T.  Three barriers.
+// Bins are ranked from the top (bin kBins-1 first); thread t owns the
+// kBins/T bins just below kBins - t*kBins/T, given in h[] (lowest first).
+// Finds the bin holding the element of rank `want` (1-based, from the top)
+// and the rank of that element inside its bin; every thread returns both.
+// Three barriers.
 template <int T>
-__device__ __forceinline__ void select_bin(const uint32_t* hist, uint32_t want, uint32_t* part,
-                                           uint32_t* sel, uint32_t& bin, uint32_t& rank) {
+__device__ __forceinline__ void select_bin_regs(const uint32_t (&h)[kBins / T], uint32_t want,
+                                                uint32_t* part, uint32_t* sel, uint32_t& bin,
+                                                uint32_t& rank) {
     constexpr int BPT = kBins / T;
     static_assert(BPT >= 1 && BPT * T == kBins, "bins per thread");
     const int base = kBins - (threadIdx.x + 1) * BPT;
-    uint32_t h[BPT];
     uint32_t sum = 0;
 #pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-        h[q] = hist[base + q];
-        sum += h[q];
-    }
+    for (int q = 0; q < BPT; ++q) sum += h[q];
     const uint32_t incl = block_inclusive_sum<T>(sum, part);
     uint32_t acc = incl - sum;
     if (acc < want && want <= incl) {
@@ -393,34 +139,37 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, uint32_t want, 
     rank = sel[1];
 }
 
-enum SegMode { kSegRows = 0, kSegChunks = 1, kSegMerge = 2 };
+// This thread's bins of a histogram (LDS or global), for select_bin_regs.
+template <int T>
+__device__ __forceinline__ void load_bins(const uint32_t* hist, uint32_t (&h)[kBins / T]) {
+    constexpr int BPT = kBins / T;
+    const int base = kBins - (threadIdx.x + 1) * BPT;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) h[q] = hist[base + q];
+}
 
-struct RegArgs {
+template <int T>
+__device__ __forceinline__ void select_bin(const uint32_t* hist, uint32_t want, uint32_t* part,
+                                           uint32_t* sel, uint32_t& bin, uint32_t& rank) {
+    uint32_t h[kBins / T];
+    load_bins<T>(hist, h);
+    select_bin_regs<T>(h, want, part, sel, bin, rank);
+}
+
+struct RowArgs {
     const float* logits;
     int64_t row_stride;
     const int32_t* lengths;
     int64_t cols;
     int32_t k;
-    int32_t chunk;           // kSegChunks / kSegMerge: logits per chunk (> k, multiple of 4)
-    int32_t chunks;          // chunks per row
     int32_t* out;            // [rows, k]
-    float* ws_val;           // [rows, chunks, k]
-    int32_t* ws_idx;         // [rows, chunks, k]
 };
-
-__device__ __forceinline__ int64_t row_length(const RegArgs& a, int64_t r) {
-    if (!a.lengths) return a.cols;
-    const int64_t l = a.lengths[r];
-    return l < 0 ? 0 : (l < a.cols ? l : a.cols);
-}
 
 constexpr int kCand = 1024;   // B1 logits kept in an LDS list (more: they stay in registers)
 
-// MODE kSegRows: one segment per row.  kSegChunks: one per (row, chunk), top-k
-// values and global indices go to the workspace.  kSegMerge: one per row over
-// the chunk results of its row.  T threads, V logits per thread (V % 4 == 0).
-template <int MODE, int T, int V>
-__global__ __launch_bounds__(T) void topk_reg_kernel(RegArgs a) {
+// One workgroup per row of at most T * V logits (V % 4 == 0).
+template <int T, int V>
+__global__ __launch_bounds__(T) void topk_row_kernel(RowArgs a) {
     static_assert(V % 4 == 0 && V <= 32, "V");
     constexpr int W = T / 64;
     __shared__ uint32_t hist0[kBins + 64];   // coarse bins, then radix digits; 64 spare bins
@@ -436,91 +185,32 @@ __global__ __launch_bounds__(T) void topk_reg_kernel(RegArgs a) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int32_t k = a.k;
-
-    // ---- the segment
-    int64_t r, len;
-    const float* src;
-    int32_t* dst = nullptr;
-    float* wv = nullptr;
-    int32_t* wi = nullptr;
-    const int32_t* map = nullptr;
-    int64_t idx_base = 0;
-    if (MODE == kSegChunks) {
-        r = blockIdx.x / a.chunks;
-        const int64_t j = blockIdx.x - r * a.chunks;
-        const int64_t lr = row_length(a, r);
-        if (lr <= k) return;                    // the merge launch writes such rows
-        idx_base = j * a.chunk;
-        len = lr - idx_base;
-        if (len <= 0) return;
-        if (len > a.chunk) len = a.chunk;
-        src = a.logits + r * a.row_stride + idx_base;
-        wv = a.ws_val + (r * a.chunks + j) * k;
-        wi = a.ws_idx + (r * a.chunks + j) * k;
-        if (len <= k) {                         // the whole chunk is a candidate
-            for (int64_t p = tid; p < len; p += T) {
-                wv[p] = src[p];
-                wi[p] = (int32_t)(idx_base + p);
-            }
-            return;
-        }
-    } else {
-        r = blockIdx.x;
-        const int64_t lr = row_length(a, r);
-        dst = a.out + r * (int64_t)k;
-        if (lr <= k) {
-            for (int64_t i = tid; i < k; i += T) dst[i] = i < lr ? (int32_t)i : -1;
-            return;
-        }
-        if (MODE == kSegRows) {
-            len = lr;
-            src = a.logits + r * a.row_stride;
-        } else {
-            // full chunks give k candidates each; the last one min(k, rest)
-            const int64_t full = lr / a.chunk, rest = lr - full * a.chunk;
-            len = full * k + (rest < k ? rest : k);
-            src = a.ws_val + r * a.chunks * (int64_t)k;
-            map = a.ws_idx + r * a.chunks * (int64_t)k;
-            if (len <= k) {
-                for (int64_t i = tid; i < k; i += T) dst[i] = i < len ? map[i] : -1;
-                return;
-            }
-        }
+    const int64_t r = blockIdx.x;
+    int64_t len = a.cols;
+    if (a.lengths) {
+        const int64_t l = a.lengths[r];
+        len = l < 0 ? 0 : (l < a.cols ? l : a.cols);
     }
+    int32_t* dst = a.out + r * (int64_t)k;
+    if (len <= k) {
+        for (int64_t i = tid; i < k; i += T) dst[i] = i < len ? (int32_t)i : -1;
+        return;
+    }
+    const float* src = a.logits + r * a.row_stride;
     const int32_t n = (int32_t)len;          // <= T * V, checked on the host
 
     // Slot i of thread t holds logit pos(i); live(i) is false (for the whole
-    // workgroup) when no thread's slot i is inside the segment.
-    auto pos = [&](int i) -> int32_t {
-        if (MODE == kSegMerge) return tid + i * T;
-        return 4 * (tid + (i >> 2) * T) + (i & 3);
-    };
-    auto live = [&](int i) -> bool {
-        if (MODE == kSegMerge) return i * T < n;
-        return (i >> 2) * T * 4 < n;
-    };
-    auto write = [&](uint32_t slot, int32_t p, float v) {
-        if (slot >= (uint32_t)k) return;
-        if (MODE == kSegRows) {
-            dst[slot] = p;
-        } else if (MODE == kSegChunks) {
-            wv[slot] = v;
-            wi[slot] = (int32_t)(idx_base + p);
-        } else {
-            dst[slot] = map[p];
-        }
+    // workgroup) when no thread's slot i is inside the row.
+    auto pos = [&](int i) -> int32_t { return 4 * (tid + (i >> 2) * T) + (i & 3); };
+    auto live = [&](int i) -> bool { return (i >> 2) * T * 4 < n; };
+    auto write = [&](uint32_t slot, int32_t p) {
+        if (slot < (uint32_t)k) dst[slot] = p;
     };
 
     // ---- load, as order keys; key 0 marks a slot outside the segment (no
     // logit that is not NaN has key 0)
     uint32_t key[V];
-    if (MODE == kSegMerge) {
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int32_t p = pos(i);
-            key[i] = (live(i) && p < n) ? order_key(src[p]) : 0u;
-        }
-    } else {
+    {
         const float4* s4 = reinterpret_cast<const float4*>(src);
 #pragma unroll
         for (int j = 0; j < V / 4; ++j) {
@@ -621,7 +311,7 @@ __global__ __launch_bounds__(T) void topk_reg_kernel(RegArgs a) {
         uint32_t o = block_inclusive_sum<T>(n_gt, part) - n_gt;
 #pragma unroll
         for (int i = 0; i < V; ++i)
-            if (live(i) && key[i] && bin_at(i) > b1) write(o++, pos(i), key_value(key[i]));
+            if (live(i) && key[i] && bin_at(i) > b1) write(o++, pos(i));
     }
     const uint32_t above0 = (uint32_t)k - rem0;  // slots taken by the bins above B1
     const bool listed = n1 <= (uint32_t)kCand;
@@ -636,7 +326,7 @@ __global__ __launch_bounds__(T) void topk_reg_kernel(RegArgs a) {
                 const uint32_t kj = cand_key[j];
                 rank += (kj > key || (kj == key && j < (uint32_t)lane)) ? 1u : 0u;
             }
-            if (mine && rank < rem0) write(above0 + rank, cand_pos[lane], key_value(key));
+            if (mine && rank < rem0) write(above0 + rank, cand_pos[lane]);
         }
         return;
     }
@@ -701,130 +391,343 @@ __global__ __launch_bounds__(T) void topk_reg_kernel(RegArgs a) {
     const uint32_t above = (uint32_t)k - rem;
     for_b1([&](uint32_t key, int32_t p) {
         if (key > kth) {
-            write(above0 + atomicAdd(&cnt[1], 1u), p, key_value(key));
+            write(above0 + atomicAdd(&cnt[1], 1u), p);
         } else if (key == kth) {
             const uint32_t q = atomicAdd(&cnt[2], 1u);
-            if (q < rem) write(above + q, p, key_value(key));
+            if (q < rem) write(above + q, p);
         }
     });
+}
+
+
+// ------------------------------------------------------ split-row path ----
+// Rows spread over one workgroup per chunk of 4096 logits, in four
+// dispatches over a caller workspace (the dispatch boundaries make each
+// step's global writes visible to the next; no fences or waits in kernels):
+//   zero:   the row's two 2048-bin histograms and counters;
+//   hist:   each chunk adds the histogram of its keys' top 11 bits (digit 1);
+//   select: each chunk finds the bin B1 of the k-th largest from the row's
+//           histogram, writes its logits above B1 at slots taken with one
+//           global atomic per workgroup, appends its B1 logits (key and index)
+//           to the row's list and adds their next 11 bits (digit 2) to the
+//           second histogram;
+//   finish: one workgroup per row finds digit 2 from the second histogram and
+//           the last 10 bits from an LDS histogram over the list, and writes
+//           the list's selected entries.
+constexpr int kSplitT = 256;
+constexpr int kSplitV = 16;
+constexpr int kSplitChunk = kSplitT * kSplitV;
+constexpr int kStateWords = 2 * kBins + 8;    // two histograms, counters: placed, listed
+
+struct SplitArgs {
+    const float* logits;
+    int64_t row_stride;
+    const int32_t* lengths;
+    int64_t cols;
+    int32_t k;
+    int32_t chunks;        // per row: ceil(cols / kSplitChunk)
+    int32_t* out;          // [rows, k]
+    uint32_t* state;       // [rows, kStateWords]
+    uint32_t* list_key;    // [rows, list_stride]
+    int32_t* list_pos;     // [rows, list_stride]
+    int64_t list_stride;   // >= cols
+};
+
+__device__ __forceinline__ int64_t split_row_length(const SplitArgs& a, int64_t r) {
+    if (!a.lengths) return a.cols;
+    const int64_t l = a.lengths[r];
+    return l < 0 ? 0 : (l < a.cols ? l : a.cols);
+}
+
+// Keys of logits [0, n) of a chunk; slot i of thread t is logit
+// 4 * (t + (i / 4) * kSplitT) + i % 4; key 0 marks a slot past n.
+__device__ __forceinline__ void load_chunk_keys(const float* src, int32_t n, uint32_t (&key)[kSplitV]) {
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int j = 0; j < kSplitV / 4; ++j) {
+        const int32_t c = threadIdx.x + j * kSplitT;
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (4 * c < n) f = s4[c];
+        key[4 * j + 0] = 4 * c + 0 < n ? order_key(f.x) : 0u;
+        key[4 * j + 1] = 4 * c + 1 < n ? order_key(f.y) : 0u;
+        key[4 * j + 2] = 4 * c + 2 < n ? order_key(f.z) : 0u;
+        key[4 * j + 3] = 4 * c + 3 < n ? order_key(f.w) : 0u;
+    }
+}
+
+__device__ __forceinline__ int32_t chunk_pos(int i) {
+    return 4 * (threadIdx.x + (i >> 2) * kSplitT) + (i & 3);
+}
+
+__global__ __launch_bounds__(kSplitT) void topk_split_zero_kernel(SplitArgs a) {
+    uint32_t* st = a.state + blockIdx.x * (int64_t)kStateWords;
+    for (int i = threadIdx.x; i < kStateWords; i += kSplitT) st[i] = 0;
+}
+
+// The digit-1 histogram uses the selection's chunks; chunks of 16384 logits
+// (1024 threads) measured slower: fewer workgroups to overlap, more LDS
+// contention in each.
+__global__ __launch_bounds__(kSplitT) void topk_split_hist_kernel(SplitArgs a) {
+    __shared__ uint32_t hist[kBins];
+    const int64_t r = blockIdx.x / a.chunks;
+    const int64_t base = (blockIdx.x - r * a.chunks) * (int64_t)kSplitChunk;
+    const int64_t lr = split_row_length(a, r);
+    if (lr <= a.k || base >= lr) return;
+    const int32_t n = (int32_t)(lr - base < kSplitChunk ? lr - base : kSplitChunk);
+    for (int b = threadIdx.x; b < kBins; b += kSplitT) hist[b] = 0;
+    uint32_t key[kSplitV];
+    load_chunk_keys(a.logits + r * a.row_stride + base, n, key);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSplitV; ++i)
+        if (key[i]) atomicAdd(&hist[key[i] >> 21], 1u);
+    __syncthreads();
+    uint32_t* g1 = a.state + r * kStateWords;
+    for (int b = threadIdx.x; b < kBins; b += kSplitT) {
+        const uint32_t c = hist[b];
+        if (c) atomicAdd(&g1[b], c);
+    }
+}
+
+__global__ __launch_bounds__(kSplitT) void topk_split_select_kernel(SplitArgs a) {
+    constexpr int T = kSplitT;
+    constexpr int W = T / 64;
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t part[W];
+    __shared__ uint32_t sel[2];
+    __shared__ uint32_t shared_base[2];
+
+    const int tid = threadIdx.x;
+    const int32_t k = a.k;
+    const int64_t r = blockIdx.x / a.chunks;
+    const int64_t j = blockIdx.x - r * a.chunks;
+    const int64_t lr = split_row_length(a, r);
+    int32_t* dst = a.out + r * (int64_t)k;
+    if (lr <= k) {
+        if (j == 0)
+            for (int64_t i = tid; i < k; i += T) dst[i] = i < lr ? (int32_t)i : -1;
+        return;
+    }
+    const int64_t base = j * kSplitChunk;
+    if (base >= lr) return;
+    const int32_t n = (int32_t)(lr - base < kSplitChunk ? lr - base : kSplitChunk);
+    uint32_t* g1 = a.state + r * kStateWords;
+    uint32_t* g2 = g1 + kBins;
+    uint32_t* ctrl = g2 + kBins;
+    uint32_t* lk = a.list_key + r * a.list_stride;
+    int32_t* lp = a.list_pos + r * a.list_stride;
+
+    for (int b = tid; b < kBins; b += T) hist[b] = 0;
+    if (tid == 0) {
+        sel[0] = 0;
+        sel[1] = 1;
+    }
+    uint32_t key[kSplitV];
+    load_chunk_keys(a.logits + r * a.row_stride + base, n, key);
+    uint32_t h1[kBins / T];
+    load_bins<T>(g1, h1);
+
+    // B1 and the rank in it, from the row's digit-1 histogram
+    uint32_t b1, rem;
+    select_bin_regs<T>(h1, (uint32_t)k, part, sel, b1, rem);
+    b1 = min(b1, (uint32_t)(kBins - 1));
+
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < kSplitV; ++i) {
+        if (key[i]) {
+            const uint32_t d1 = key[i] >> 21;
+            n_gt += d1 > b1 ? 1u : 0u;
+            if (d1 == b1) {
+                ++n_eq;
+                atomicAdd(&hist[(key[i] >> 10) & (kBins - 1)], 1u);
+            }
+        }
+    }
+    const uint32_t packed = n_gt | (n_eq << 16);             // chunk totals < 2^13
+    const uint32_t excl = block_inclusive_sum<T>(packed, part) - packed;
+    if (tid == 0) {
+        uint32_t tot = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) tot += part[w];
+        // both running counts in one 64-bit word: placed (low), listed (high)
+        const unsigned long long old = atomicAdd(reinterpret_cast<unsigned long long*>(ctrl),
+                                                 (unsigned long long)(tot & 0xFFFFu) |
+                                                     ((unsigned long long)(tot >> 16) << 32));
+        shared_base[0] = (uint32_t)old;
+        shared_base[1] = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+    uint32_t og = shared_base[0] + (excl & 0xFFFFu);
+    uint32_t oe = shared_base[1] + (excl >> 16);
+#pragma unroll
+    for (int i = 0; i < kSplitV; ++i) {
+        if (key[i]) {
+            const uint32_t d1 = key[i] >> 21;
+            if (d1 > b1) {
+                if (og < (uint32_t)k) dst[og] = (int32_t)(base + chunk_pos(i));
+                ++og;
+            } else if (d1 == b1) {
+                if (oe < (uint64_t)a.list_stride) {
+                    lk[oe] = key[i];
+                    lp[oe] = (int32_t)(base + chunk_pos(i));
+                }
+                ++oe;
+            }
+        }
+    }
+    for (int b = tid; b < kBins; b += T) {
+        const uint32_t c = hist[b];
+        if (c) atomicAdd(&g2[b], c);
+    }
+}
+
+// One workgroup per row: rank `rem` among the n1 listed B1 logits, from the
+// digit-2 histogram and an LDS histogram of the last 10 bits.
+constexpr int kFinishT = 1024;
+
+__global__ __launch_bounds__(kFinishT) void topk_split_finish_kernel(SplitArgs a) {
+    constexpr int T = kFinishT;
+    constexpr int W = T / 64;
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t part[W];
+    __shared__ uint32_t sel[2];
+    __shared__ uint32_t cnt[2];
+
+    const int tid = threadIdx.x;
+    const int32_t k = a.k;
+    const int64_t r = blockIdx.x;
+    if (split_row_length(a, r) <= k) return;
+    int32_t* dst = a.out + r * (int64_t)k;
+    const uint32_t* g1 = a.state + r * kStateWords;
+    const uint32_t* g2 = g1 + kBins;
+    const uint32_t* lk = a.list_key + r * a.list_stride;
+    const int32_t* lp = a.list_pos + r * a.list_stride;
+
+    for (int b = tid; b < kBins; b += T) hist[b] = 0;
+    if (tid < 2) cnt[tid] = 0;
+    if (tid == 0) {
+        sel[0] = 0;
+        sel[1] = 1;
+    }
+    uint32_t h1[kBins / T], h2[kBins / T];
+    load_bins<T>(g1, h1);
+    load_bins<T>(g2, h2);
+    uint32_t b1, rem, b2, rem2, b3, rem3;
+    select_bin_regs<T>(h1, (uint32_t)k, part, sel, b1, rem);
+    b1 = min(b1, (uint32_t)(kBins - 1));
+    const uint32_t n1 = min(g1[b1], (uint32_t)a.list_stride);
+    const uint32_t above1 = (uint32_t)k - rem;
+    select_bin_regs<T>(h2, rem, part, sel, b2, rem2);
+    b2 = min(b2, (uint32_t)(kBins - 1));
+    for (uint32_t c = tid; c < n1; c += T) {
+        const uint32_t kk = lk[c];
+        if (((kk >> 10) & (kBins - 1)) == b2) atomicAdd(&hist[kk & 1023u], 1u);
+    }
+    __syncthreads();
+    select_bin<T>(hist, rem2, part, sel, b3, rem3);
+    const uint32_t kth = (b1 << 21) | (b2 << 10) | (b3 & 1023u);
+    const uint32_t above = (uint32_t)k - rem3;
+    for (uint32_t c = tid; c < n1; c += T) {
+        const uint32_t kk = lk[c];
+        if (kk > kth) {
+            const uint32_t slot = above1 + atomicAdd(&cnt[0], 1u);
+            if (slot < (uint32_t)k) dst[slot] = lp[c];
+        } else if (kk == kth) {
+            const uint32_t q = atomicAdd(&cnt[1], 1u);
+            if (q < rem3) dst[above + q] = lp[c];
+        }
+    }
 }
 
 }  // namespace
 
 // Kernel choice for a call; topk_workspace_bytes and launch_topk share it.
 struct TopkPlan {
-    int kind;          // 0: one register-resident launch per row, 1: chunks + merge, 2: generic
-    int variant;       // kind 0: row shape 0..3;  kind 1: merge shape 0..2
-    int64_t chunks;    // kind 1: chunks per row
-    int64_t ws_bytes;  // kind 1: workspace bytes
+    int split;         // 0: one row kernel launch, 1: the split-row path
+    int variant;       // row kernel shape 0..3
+    int64_t chunks;    // split: chunks of kSplitChunk per row
+    int64_t ws_bytes;  // split: workspace bytes
 };
 
-// Workgroup shapes (threads x logits per thread) of the one-pass row kernel
-// for rows of up to 4096, 8192, 16384 and 32768 logits.
-#ifndef DSAIDX_TOPK_R4K
+// Workgroup shapes (threads, logits per thread) of the row kernel for rows of
+// up to 4096, 8192, 16384 and 32768 logits.
 #define DSAIDX_TOPK_R4K 256, 16
-#endif
-#ifndef DSAIDX_TOPK_R8K
 #define DSAIDX_TOPK_R8K 512, 16
-#endif
-#ifndef DSAIDX_TOPK_R16K
 #define DSAIDX_TOPK_R16K 1024, 16
-#endif
-#ifndef DSAIDX_TOPK_R32K
 #define DSAIDX_TOPK_R32K 1024, 32
-#endif
-// Longest row of the one-pass path; longer rows go through chunks.
-#ifndef DSAIDX_TOPK_ONE_PASS_MAX
-#define DSAIDX_TOPK_ONE_PASS_MAX 32768
-#endif
-#ifndef DSAIDX_TOPK_CHUNK_T
-#define DSAIDX_TOPK_CHUNK_T 1024
-#endif
-#ifndef DSAIDX_TOPK_CHUNK_V
-#define DSAIDX_TOPK_CHUNK_V 16
-#endif
-constexpr int64_t kChunk = int64_t(DSAIDX_TOPK_CHUNK_T) * DSAIDX_TOPK_CHUNK_V;
-constexpr int64_t kMergeMax = 1024 * 32;   // candidates per row the merge takes
+constexpr int64_t kRowMax = 32768;       // longest row of the row kernel
 
-template <int T, int V>
-constexpr int64_t cap() { return int64_t(T) * V; }
-
-static TopkPlan plan_topk(int64_t rows, int64_t cols, int32_t k) {
-    TopkPlan p{2, 0, 0, 0};
-    if (cols <= DSAIDX_TOPK_ONE_PASS_MAX) {
-        p.kind = 0;
-        p.variant = cols <= cap<DSAIDX_TOPK_R4K>() ? 0
-                  : cols <= cap<DSAIDX_TOPK_R8K>() ? 1
-                  : cols <= cap<DSAIDX_TOPK_R16K>() ? 2 : 3;
+static TopkPlan plan_topk(int64_t rows, int64_t cols, int32_t) {
+    TopkPlan p{0, 0, 0, 0};
+    if (cols <= kRowMax) {
+        p.variant = cols <= 4096 ? 0 : (cols <= 8192 ? 1 : (cols <= 16384 ? 2 : 3));
         return p;
     }
-    const int64_t chunks = (cols + kChunk - 1) / kChunk;
-    if (k < kChunk && chunks * k <= kMergeMax && rows * chunks < (int64_t(1) << 31)) {
-        p.kind = 1;
-        p.variant = chunks * k <= 8192 ? 0 : (chunks * k <= 16384 ? 1 : 2);
-        p.chunks = chunks;
-        p.ws_bytes = rows * chunks * (int64_t)k * 8;
+    p.split = 1;
+    p.chunks = (cols + kSplitChunk - 1) / kSplitChunk;
+    // the grid holds rows * chunks workgroups; that bound also keeps the
+    // workspace size far inside int64
+    if (rows * p.chunks >= (int64_t(1) << 31)) {
+        p.ws_bytes = -1;
+        return p;
     }
+    p.ws_bytes = rows * (int64_t(kStateWords) * 4 + 8 * ((cols + 3) / 4 * 4));
     return p;
 }
-static_assert(cap<DSAIDX_TOPK_R4K>() >= 4096 && cap<DSAIDX_TOPK_R8K>() >= 8192 &&
-                  cap<DSAIDX_TOPK_R16K>() >= 16384 && cap<DSAIDX_TOPK_R32K>() >= 32768 &&
-                  DSAIDX_TOPK_ONE_PASS_MAX <= 32768,
-              "row shapes must cover their row lengths");
 
 int64_t topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k) {
     return plan_topk(rows, cols, k).ws_bytes;
 }
 
-template <int MODE, int T, int V>
-static hipError_t launch_reg(RegArgs& a, int64_t grid, hipStream_t stream) {
+template <int T, int V>
+static hipError_t launch_row(RowArgs& a, int64_t rows, hipStream_t stream) {
+    static_assert(T * V >= 4096, "row shape");
     void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&topk_reg_kernel<MODE, T, V>),
-                           dim3((unsigned)grid), dim3(T), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&topk_row_kernel<T, V>),
+                           dim3((unsigned)rows), dim3(T), args, 0, stream);
 }
 
 hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* lengths,
                        int64_t rows, int64_t cols, int32_t k, int32_t* out, void* workspace,
                        hipStream_t stream) {
     const TopkPlan p = plan_topk(rows, cols, k);
-    if (p.kind == 2) {
-        void* args[] = {&logits, &row_stride, &lengths, &cols, &k, &out};
-        const void* fn;
-        if (cols <= 8192)
-            fn = reinterpret_cast<const void*>(&topk_generic_kernel<8192, 2048>);
-        else if (cols <= 24576)
-            fn = reinterpret_cast<const void*>(&topk_generic_kernel<24576, 4096>);
-        else
-            fn = reinterpret_cast<const void*>(&topk_generic_kernel<0, 16384>);
-        return hipLaunchKernel(fn, dim3((unsigned)rows), dim3(kThreads), args, 0, stream);
-    }
-    RegArgs a{};
-    a.logits = logits;
-    a.row_stride = row_stride;
-    a.lengths = lengths;
-    a.cols = cols;
-    a.k = k;
-    a.out = out;
-    if (p.kind == 0) {
+    if (!p.split) {
+        RowArgs a{logits, row_stride, lengths, cols, k, out};
         switch (p.variant) {
-            case 0: return launch_reg<kSegRows, DSAIDX_TOPK_R4K>(a, rows, stream);
-            case 1: return launch_reg<kSegRows, DSAIDX_TOPK_R8K>(a, rows, stream);
-            case 2: return launch_reg<kSegRows, DSAIDX_TOPK_R16K>(a, rows, stream);
-            default: return launch_reg<kSegRows, DSAIDX_TOPK_R32K>(a, rows, stream);
+            case 0: return launch_row<DSAIDX_TOPK_R4K>(a, rows, stream);
+            case 1: return launch_row<DSAIDX_TOPK_R8K>(a, rows, stream);
+            case 2: return launch_row<DSAIDX_TOPK_R16K>(a, rows, stream);
+            default: return launch_row<DSAIDX_TOPK_R32K>(a, rows, stream);
         }
     }
-    a.chunk = (int32_t)kChunk;
-    a.chunks = (int32_t)p.chunks;
-    a.ws_val = static_cast<float*>(workspace);
-    a.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.ws_bytes / 2);
-    const hipError_t e =
-        launch_reg<kSegChunks, DSAIDX_TOPK_CHUNK_T, DSAIDX_TOPK_CHUNK_V>(a, rows * p.chunks, stream);
-    if (e != hipSuccess) return e;
-    switch (p.variant) {
-        case 0: return launch_reg<kSegMerge, 512, 16>(a, rows, stream);
-        case 1: return launch_reg<kSegMerge, 1024, 16>(a, rows, stream);
-        default: return launch_reg<kSegMerge, 1024, 32>(a, rows, stream);
-    }
+    SplitArgs sa{};
+    sa.logits = logits;
+    sa.row_stride = row_stride;
+    sa.lengths = lengths;
+    sa.cols = cols;
+    sa.k = k;
+    sa.chunks = (int32_t)p.chunks;
+    sa.out = out;
+    const int64_t colsp = (cols + 3) / 4 * 4;
+    sa.state = static_cast<uint32_t*>(workspace);
+    sa.list_key = sa.state + rows * kStateWords;
+    sa.list_pos = reinterpret_cast<int32_t*>(sa.list_key + rows * colsp);
+    sa.list_stride = colsp;
+    void* args[] = {&sa};
+    const dim3 grid((unsigned)(rows * p.chunks));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_zero_kernel),
+                                   dim3((unsigned)rows), dim3(kSplitT), args, 0, stream);
+    if (e == hipSuccess)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_hist_kernel), grid,
+                            dim3(kSplitT), args, 0, stream);
+    if (e == hipSuccess)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_select_kernel), grid,
+                            dim3(kSplitT), args, 0, stream);
+    if (e == hipSuccess)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_finish_kernel),
+                            dim3((unsigned)rows), dim3(kFinishT), args, 0, stream);
+    return e;
 }
 
 }  // namespace dsaidx

@@ -218,11 +218,15 @@ def test_topk_workspace_size_and_checks(L):
     ws = L.dsaidx_topk_workspace_bytes
     assert ws(64, 16384, 2048) == 0
     assert ws(64, 32768, 2048) == 0
-    assert ws(64, 131072, 2048) == 64 * 8 * 2048 * 8
-    assert ws(3, 32769, 7) == 3 * 3 * 7 * 8
-    assert ws(64, 50000, 12000) == 0          # k too large for the chunked path
+    # rows longer than 32768: per row two 2048-bin histograms and counters
+    # (16416 bytes) and a list of up to cols (key, index) pairs
+    assert ws(64, 131072, 2048) == 64 * (16416 + 8 * 131072)
+    assert ws(3, 32769, 7) == 3 * (16416 + 8 * 32772)
+    assert ws(64, 50000, 40000) == 64 * (16416 + 8 * 50000)
     assert ws(0, 131072, 2048) == 0
     assert ws(-1, 10, 1) == -1 and ws(1, 10, 0) == -1 and ws(1, -1, 1) == -1
+    assert ws(1 << 20, 1 << 30, 8) == -1      # grid of rows * ceil(cols / 4096) workgroups too large
+    assert ws((1 << 31) - 1, 32768, 8) == 0
     need = ws(2, 131072, 2048)
 
     def call(w, nbytes, rows=2, cols=131072):
@@ -232,3 +236,4 @@ def test_topk_workspace_size_and_checks(L):
     assert call(FAKE, need - 1) == B.DSAIDX_ERR_INVALID_ARGUMENT
     assert call(FAKE + 4, need) == B.DSAIDX_ERR_INVALID_ARGUMENT
     assert call(None, 0, rows=0) == B.DSAIDX_OK
+    assert call(FAKE, 1 << 62, rows=1 << 20, cols=1 << 30) == B.DSAIDX_ERR_INVALID_ARGUMENT

@@ -153,7 +153,7 @@ def test_degenerate_value_ranges():
 ])
 def test_launch_variants(rows, cols, k, lengths, ws):
     wl = W.topk_make(rows, cols, k=k, lengths=lengths, seed=cols + k)
-    assert (R.dsaidx_topk_workspace_bytes(rows, cols, k) > 0) == bool(ws)
+    assert (R.dsaidx_topk_workspace_bytes(rows, cols, k) > 0) == (cols > 32768)
     out = run_topk(wl.logits, k, wl.lengths)
     check(out, wl.logits, k, wl.lengths)
 
@@ -173,7 +173,7 @@ def test_workspace_reuse_and_too_small():
     rows, cols, k = 4, 100000, 2048
     wl = W.topk_make(rows, cols, k=k, lengths="ragged", seed=5)
     need = R.dsaidx_topk_workspace_bytes(rows, cols, k)
-    assert need == rows * 7 * k * 8
+    assert need > 0
     d = torch.from_numpy(wl.logits).cuda()
     dl = torch.from_numpy(wl.lengths).cuda()
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
@@ -184,3 +184,69 @@ def test_workspace_reuse_and_too_small():
         check(out.cpu().numpy(), wl.logits, k, wl.lengths)
     with pytest.raises(R.DsaidxError):
         R.dsaidx_topk_per_row(d, k, out, dl, workspace=ws[: need - 16])
+
+
+def test_long_rows_chunk_edges_and_extreme_k():
+    """Rows longer than 32768 logits: lengths on and around 4096-logit chunk
+    edges, k = 1 and k = len - 1."""
+    rows, cols = 8, 40960
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    lens = np.array([4095, 4096, 4097, 8192, 32768, 32769, 40959, 40960], np.int32)
+    for k in (1, 2048, 4094):
+        out = run_topk(x, k, lens)
+        check(out, x, k, lens)
+    k = 40959
+    out = run_topk(x[:1], k, None)
+    check(out, x[:1], k, None)
+
+
+def test_long_rows_degenerate_values():
+    """Long rows whose k-th value sits in one crowded bin: every logit equal,
+    a few distinct values, -inf masses and values in a narrow range."""
+    rows, cols, k = 5, 50000, 2048
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[0] = 1.5
+    x[1] = np.round(x[1])
+    x[2] = -np.inf
+    x[2, 7000:9500] = rng.standard_normal(2500).astype(np.float32)
+    x[3] = (1.0 + 0.1 * rng.random(cols)).astype(np.float32)
+    x[4, ::3] = -0.0
+    x[4, 1::3] = 0.0
+    out = run_topk(x, k)
+    check(out, x, k)
+
+
+def test_split_path_under_graph_replay():
+    """The four dispatches of a long-row call captured in one HIP graph and
+    replayed, with new logits copied in and eager calls between replays;
+    every replay is checked."""
+    rows, cols, k = 6, 50000, 2048
+    d = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    dl = torch.empty(rows, dtype=torch.int32, device="cuda")
+    out = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(R.dsaidx_topk_workspace_bytes(rows, cols, k), dtype=torch.uint8, device="cuda")
+    wl0 = W.topk_make(rows, cols, k=k, lengths="ragged", seed=50)
+    d.copy_(torch.from_numpy(wl0.logits))
+    dl.copy_(torch.from_numpy(wl0.lengths))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        R.dsaidx_topk_per_row(d, k, out, dl, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        R.dsaidx_topk_per_row(d, k, out, dl, workspace=ws)
+    other = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    for rep in range(4):
+        wl = W.topk_make(rows, cols, k=k, lengths="ragged", seed=51 + rep)
+        d.copy_(torch.from_numpy(wl.logits))
+        dl.copy_(torch.from_numpy(wl.lengths))
+        g.replay()
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), wl.logits, k, wl.lengths)
+        R.dsaidx_topk_per_row(d[:3], k, other[:3], dl[:3], workspace=ws)   # eager, same workspace
+        torch.cuda.synchronize()
+        check(other[:3].cpu().numpy(), wl.logits[:3], k, wl.lengths[:3])
