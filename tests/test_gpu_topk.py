@@ -250,3 +250,19 @@ def test_split_path_under_graph_replay():
         R.dsaidx_topk_per_row(d[:3], k, other[:3], dl[:3], workspace=ws)   # eager, same workspace
         torch.cuda.synchronize()
         check(other[:3].cpu().numpy(), wl.logits[:3], k, wl.lengths[:3])
+
+
+@pytest.mark.parametrize("shift", [5.0, -5.0])
+def test_rows_that_mislead_a_strided_sample(shift):
+    """Logits at every fourth column drawn far below (or above) the rest: an
+    estimate of the k-th largest taken from those columns misses, and the
+    exact selection must still come out."""
+    rows, k = 6, 2048
+    for cols in (4096, 8192, 16384, 32768):
+        rng = np.random.default_rng(cols)
+        x = rng.standard_normal((rows, cols)).astype(np.float32)
+        x[:, 0::4] -= shift
+        x[:, 1::4] += shift
+        lens = np.array([cols, cols - 1, cols // 2 + 3, k + 1, k + 5, 3 * cols // 4], np.int32)
+        out = run_topk(x, k, lens)
+        check(out, x, k, lens)
