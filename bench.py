@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+WARM_MS = 100.0      # warm-up of every secondary measurement (GPU clock ramp)
 KERNEL_SOURCES = [os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", f)
                   for f in ("dsaidx_kernels.hip", "dsaidx_internal.h", "dsaidx_api.cpp")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_indexer_qk_prep_long_prefill_T65536.txt")
@@ -92,13 +93,27 @@ class Case:
         self.rope = R.rope_args(self.cos, self.sin, wl.rope_dim, wl.style)
 
 
-def time_calls(torch, fn, steps, warmup):
+def warm_up(torch, fn, warm_ms):
+    """Call fn until at least warm_ms of wall time has passed: the GPU ramps
+    its clocks up over tens of milliseconds of load (an 8192-token call timed
+    after 20 warmup calls from idle runs about 9 % slower than warm)."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_calls(torch, fn, steps, warmup, warm_ms=0.0):
     """Mean milliseconds per call over `steps` back-to-back calls, bracketed by
-    HIP events on the stream the calls are enqueued on."""
+    HIP events on the stream the calls are enqueued on, after `warmup` calls
+    (and at least warm_ms of them, when given)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if warm_ms > 0:
+        warm_up(torch, fn, warm_ms)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -109,9 +124,9 @@ def time_calls(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def time_graph(torch, fn, calls, replays):
+def time_graph(torch, fn, calls, replays, warm_ms=100.0):
     """Mean milliseconds per call when `calls` calls are captured in one HIP
-    graph and the graph is replayed `replays` times."""
+    graph and the graph is replayed `replays` times (after warm_ms of replays)."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -124,6 +139,7 @@ def time_graph(torch, fn, calls, replays):
             fn()
     g.replay()
     torch.cuda.synchronize()
+    warm_up(torch, g.replay, warm_ms)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
@@ -167,7 +183,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode, prefill-chunk and k-only measurements")
@@ -239,7 +255,7 @@ def main():
         def fused1():
             R.dsaidx_qk_fused(c1.qa, c1.ka, c1.rope)
 
-        ms_eager = time_calls(torch, fused1, 2000, 200)
+        ms_eager = time_calls(torch, fused1, 2000, 200, WARM_MS)
         ms_graph = time_graph(torch, fused1, 100, 20)
         extras["decode_batch_T64"] = {"us_per_call_eager": ms_eager * 1e3,
                                       "us_per_call_graph": ms_graph * 1e3,
@@ -257,7 +273,7 @@ def main():
         del c1, c2, c2b
         # the same long prefill into the page-interleaved index-K cache (64-slot pages)
         cp = Case(wl, torch, R, k_flags=R.DSAIDX_K_PAGED_CACHE, page_size=64)
-        msp = time_calls(torch, lambda: R.dsaidx_qk_fused(cp.qa, cp.ka, cp.rope), 50, 5)
+        msp = time_calls(torch, lambda: R.dsaidx_qk_fused(cp.qa, cp.ka, cp.rope), 50, 5, WARM_MS)
         extras["long_prefill_T65536_paged_cache"] = {
             "us_per_call": msp * 1e3, "achieved_GBps": bytes_call / (msp * 1e-3) / 1e9,
             "frac_of_peak": bytes_call / (msp * 1e-3) / 1e9 / PEAK_HBM_GBPS}
@@ -274,7 +290,7 @@ def main():
             it[0] += 1
             R.dsaidx_qk_fused(s.qa, s.ka, s.rope)
 
-        ms3 = time_calls(torch, fused3, 200, 20)
+        ms3 = time_calls(torch, fused3, 200, 20, WARM_MS)
         b3 = W.bytes_per_call(wl3.T)
         extras["prefill_chunk_T8192"] = {"us_per_call": ms3 * 1e3, "tokens_per_s": wl3.T / (ms3 * 1e-3),
                                          "achieved_GBps": b3 / (ms3 * 1e-3) / 1e9,
@@ -291,7 +307,7 @@ def main():
             nws = R.dsaidx_topk_workspace_bytes(rows, cols, tw.k)
             ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
             mst = time_calls(torch, lambda: R.dsaidx_topk_per_row(lg, tw.k, ot, ln, workspace=ws),
-                             50, 5)
+                             50, 5, WARM_MS)
             bt = W.topk_bytes_per_call(rows, tw.lengths, tw.k)
             extras[tw.name] = {"us_per_call": mst * 1e3, "algorithmic_bytes": bt,
                                "achieved_GBps": bt / (mst * 1e-3) / 1e9,
@@ -305,7 +321,7 @@ def main():
     n = bytes_call // 2
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-    msc = time_calls(torch, lambda: dst.copy_(src), 20, 3)
+    msc = time_calls(torch, lambda: dst.copy_(src), 20, 3, WARM_MS)
     copy_gbps = 2 * n / (msc * 1e-3) / 1e9
     result.setdefault("secondary", {})["plain_copy"] = {"bytes_moved": 2 * n,
                                                          "achieved_GBps": copy_gbps}
