@@ -151,9 +151,11 @@ def time_graph(torch, fn, calls, replays, warm_ms=100.0):
     return start.elapsed_time(end) / (calls * replays)
 
 
-def cpu_baseline(wl, target_s=5.0):
-    """The oracle (as it stands) on a leading slice of the workload, all
-    allowed host cores, sized to roughly target_s seconds of wall time."""
+def cpu_baseline(wl, target_s=5.0, min_wall_s=1.2):
+    """The oracle (as it stands) on the workload, all allowed host cores (at
+    most 16): a leading slice sized to roughly target_s of wall time, repeated
+    until at least min_wall_s has passed (with 16 threads, about 10-30 s of
+    CPU work in all)."""
     import numpy as np
 
     import oracle
@@ -173,10 +175,13 @@ def cpu_baseline(wl, target_s=5.0):
     n0 = min(wl.T, 512)
     dt = run(n0)
     n = int(min(wl.T, max(n0, n0 * target_s / max(dt, 1e-6))))
-    dt = run(n)
-    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample="first %d of %d tokens of %s (Q and K sides), one pass, %.2f s wall"
-                       % (n, wl.T, wl.name, dt))
+    passes, total = 0, 0.0
+    while passes == 0 or total < min_wall_s:
+        total += run(n)
+        passes += 1
+    return dict(value=passes * n / total, unit="tokens/s", cores=cores, kind="oracle",
+                sample="first %d of %d tokens of %s (Q and K sides), %d pass(es), %.2f s wall on %d "
+                       "threads" % (n, wl.T, wl.name, passes, total, cores))
 
 
 def main():
