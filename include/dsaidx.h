@@ -248,9 +248,11 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
                                   dsaidx_stream_t stream);
 
 /* Bytes of workspace dsaidx_topk_per_row needs for this shape: 0 when
- * cols <= 32768, else rows * (16416 + 8 * cols rounded up to a multiple of 4)
- * (per row: two 2048-bin histograms and counters, and a list of up to cols
- * candidate keys and indices); -1 for a shape dsaidx_topk_per_row rejects
+ * cols <= 32768, else rows * (16416 + 8 * L) with L = max(4096, cols / 16)
+ * rounded up to a multiple of 4 (per row: two 2048-bin histograms and
+ * counters, and a list of up to L candidate keys and indices; rows whose
+ * threshold bin holds more are finished by re-reading the row); -1 for a
+ * shape dsaidx_topk_per_row rejects
  * (including rows * ceil(cols / 4096) >= 2^31 when cols > 32768). */
 int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
 

@@ -414,7 +414,9 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
 //           second histogram;
 //   finish: one workgroup per row finds digit 2 from the second histogram and
 //           the last 10 bits from an LDS histogram over the list, and writes
-//           the list's selected entries.
+//           the list's selected entries.  When B1 overflowed the list (its
+//           capacity is max(4096, cols / 16)), the finish streams the row
+//           instead: the digit-2 histogram counts every B1 logit either way.
 constexpr int kSplitT = 256;
 constexpr int kSplitV = 16;
 constexpr int kSplitChunk = kSplitT * kSplitV;
@@ -431,8 +433,14 @@ struct SplitArgs {
     uint32_t* state;       // [rows, kStateWords]
     uint32_t* list_key;    // [rows, list_stride]
     int32_t* list_pos;     // [rows, list_stride]
-    int64_t list_stride;   // >= cols
+    int64_t list_stride;   // list capacity per row
 };
+
+// List capacity per row: B1 usually holds a few percent of a row; a larger B1
+// (heavy ties, a narrow value range) is finished by streaming the row.
+__host__ __device__ constexpr int64_t split_list_cap(int64_t cols) {
+    return ((cols / 16 > 4096 ? cols / 16 : 4096) + 3) / 4 * 4;
+}
 
 __device__ __forceinline__ int64_t split_row_length(const SplitArgs& a, int64_t r) {
     if (!a.lengths) return a.cols;
@@ -617,28 +625,45 @@ __global__ __launch_bounds__(kFinishT) void topk_split_finish_kernel(SplitArgs a
     uint32_t b1, rem, b2, rem2, b3, rem3;
     select_bin_regs<T>(h1, (uint32_t)k, part, sel, b1, rem);
     b1 = min(b1, (uint32_t)(kBins - 1));
-    const uint32_t n1 = min(g1[b1], (uint32_t)a.list_stride);
+    const uint32_t n1 = g1[b1];                              // every B1 logit of the row
+    const bool listed = n1 <= (uint64_t)a.list_stride;
     const uint32_t above1 = (uint32_t)k - rem;
     select_bin_regs<T>(h2, rem, part, sel, b2, rem2);
     b2 = min(b2, (uint32_t)(kBins - 1));
-    for (uint32_t c = tid; c < n1; c += T) {
-        const uint32_t kk = lk[c];
+    // The B1 logits: from the list, or, when it overflowed, by streaming the row.
+    const int64_t lr = split_row_length(a, r);
+    const float4* row4 = reinterpret_cast<const float4*>(a.logits + r * a.row_stride);
+    auto for_b1 = [&](auto f) {
+        if (listed) {
+            for (uint32_t c = tid; c < n1; c += T) f(lk[c], lp[c]);
+        } else {
+            for (int64_t c = tid; 4 * c < lr; c += T) {
+                const float4 v = row4[c];
+                const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t kk = order_key(e[m]);
+                    if (4 * c + m < lr && (kk >> 21) == b1) f(kk, (int32_t)(4 * c + m));
+                }
+            }
+        }
+    };
+    for_b1([&](uint32_t kk, int32_t) {
         if (((kk >> 10) & (kBins - 1)) == b2) atomicAdd(&hist[kk & 1023u], 1u);
-    }
+    });
     __syncthreads();
     select_bin<T>(hist, rem2, part, sel, b3, rem3);
     const uint32_t kth = (b1 << 21) | (b2 << 10) | (b3 & 1023u);
     const uint32_t above = (uint32_t)k - rem3;
-    for (uint32_t c = tid; c < n1; c += T) {
-        const uint32_t kk = lk[c];
+    for_b1([&](uint32_t kk, int32_t pos) {
         if (kk > kth) {
             const uint32_t slot = above1 + atomicAdd(&cnt[0], 1u);
-            if (slot < (uint32_t)k) dst[slot] = lp[c];
+            if (slot < (uint32_t)k) dst[slot] = pos;
         } else if (kk == kth) {
             const uint32_t q = atomicAdd(&cnt[1], 1u);
-            if (q < rem3) dst[above + q] = lp[c];
+            if (q < rem3) dst[above + q] = pos;
         }
-    }
+    });
 }
 
 }  // namespace
@@ -676,7 +701,7 @@ static TopkPlan plan_topk(int64_t rows, int64_t cols, int32_t) {
         p.ws_bytes = -1;
         return p;
     }
-    p.ws_bytes = rows * (int64_t(kStateWords) * 4 + 8 * ((cols + 3) / 4 * 4));
+    p.ws_bytes = rows * (int64_t(kStateWords) * 4 + 8 * split_list_cap(cols));
     return p;
 }
 
@@ -713,11 +738,11 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
     sa.k = k;
     sa.chunks = (int32_t)p.chunks;
     sa.out = out;
-    const int64_t colsp = (cols + 3) / 4 * 4;
+    const int64_t cap = split_list_cap(cols);
     sa.state = static_cast<uint32_t*>(workspace);
     sa.list_key = sa.state + rows * kStateWords;
-    sa.list_pos = reinterpret_cast<int32_t*>(sa.list_key + rows * colsp);
-    sa.list_stride = colsp;
+    sa.list_pos = reinterpret_cast<int32_t*>(sa.list_key + rows * cap);
+    sa.list_stride = cap;
     void* args[] = {&sa};
     const dim3 grid((unsigned)(rows * p.chunks));
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_zero_kernel),

@@ -266,3 +266,19 @@ def test_rows_that_mislead_a_strided_sample(shift):
         lens = np.array([cols, cols - 1, cols // 2 + 3, k + 1, k + 5, 3 * cols // 4], np.int32)
         out = run_topk(x, k, lens)
         check(out, x, k, lens)
+
+
+def test_long_rows_threshold_bin_over_list_capacity():
+    """Rows longer than 32768 whose threshold bin (same top 11 key bits) holds
+    more logits than the per-row candidate list takes (max(4096, cols / 16)):
+    the selection finishes by re-reading the row."""
+    rows, cols, k = 4, 65536, 2048
+    rng = np.random.default_rng(61)
+    x = (-5.0 + 0.1 * rng.standard_normal((rows, cols))).astype(np.float32)
+    for r in range(rows):
+        idx = rng.permutation(cols)
+        x[r, idx[:5000]] = (1.0 + 0.2 * rng.random(5000)).astype(np.float32)   # one top-11-bit bin
+        x[r, idx[5000:5100]] = (3.0 + rng.random(100)).astype(np.float32)
+    lens = np.array([cols, cols - 7, 60001, 40000], np.int32)
+    out = run_topk(x, k, lens)
+    check(out, x, k, lens)
