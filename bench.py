@@ -28,6 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "fused indexer Q/K prep tokens/s and achieved HBM GB/s (% peak); \u00b5s/call"
 PEAK_HBM_GBPS = 8000.0
 WARM_MS = 100.0      # warm-up of the bandwidth-bound secondary measurements (GPU clock ramp)
 WARM_MS_LATENCY = 20.0   # the latency-bound decode ones (insensitive to it; keeps traces small)
@@ -225,7 +226,7 @@ def main():
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(src_hash)
     result = {
-        "metric": "fused indexer Q/K prep tokens/s and achieved HBM GB/s (% peak); us/call",
+        "metric": METRIC,
         "value": wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
