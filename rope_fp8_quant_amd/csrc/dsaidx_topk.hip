@@ -84,10 +84,6 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
     return op(a, b);
 }
 
-struct MinF { __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
-    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b))); } };
-struct MaxF { __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
-    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); } };
 struct MinU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
 struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
 
@@ -111,7 +107,7 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* pa
 // kBins/T bins just below kBins - t*kBins/T, given in h[] (lowest first).
 // Finds the bin holding the element of rank `want` (1-based, from the top)
 // and the rank of that element inside its bin; every thread returns both.
-// Three barriers.
+// Two barriers.
 template <int T>
 __device__ __forceinline__ void select_bin_regs(const uint32_t (&h)[kBins / T], uint32_t want,
                                                 uint32_t* part, uint32_t* sel, uint32_t& bin,
@@ -208,8 +204,8 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         if (slot < (uint32_t)k) dst[slot] = p;
     };
 
-    // ---- load, as order keys; key 0 marks a slot outside the segment (no
-    // logit that is not NaN has key 0)
+    // ---- load, as order keys; key 0 marks a slot outside the row (no logit
+    // that is not NaN has key 0)
     uint32_t key[V];
     {
         const float4* s4 = reinterpret_cast<const float4*>(src);
@@ -270,8 +266,8 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         return min((uint32_t)t, (uint32_t)(kBins - 1));
     };
 
-    // ---- 2. coarse histogram (slots outside the segment count in a spare
-    // bin of their lane) and the bin B1 of the k-th largest
+    // ---- 2. coarse histogram (slots outside the row count in a spare bin of
+    // their lane) and the bin B1 of the k-th largest
     uint32_t bins[(V + 1) / 2];
 #pragma unroll
     for (int i = 0; i < (V + 1) / 2; ++i) bins[i] = 0;
@@ -348,7 +344,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         kmn = key < kmn ? key : kmn;
         kmx = key > kmx ? key : kmx;
     });
-    for (int b = tid; b < kBins; b += T) hist0[b] = 0;       // n1 and select_bin read it before
+    for (int b = tid; b < kBins; b += T) hist0[b] = 0;       // last read before the step-3 barrier
     {
         const uint32_t wmn = wave_reduce(kmn, MinU());
         const uint32_t wmx = wave_reduce(kmx, MaxU());
