@@ -238,3 +238,51 @@ def test_topk_workspace_size_and_checks(L):
     assert call(FAKE + 4, need) == B.DSAIDX_ERR_INVALID_ARGUMENT
     assert call(None, 0, rows=0) == B.DSAIDX_OK
     assert call(FAKE, 1 << 62, rows=1 << 20, cols=1 << 30) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "dsaidx.h"
+
+int main(void) {
+    dsaidx_rope rope;
+    dsaidx_q_args q;
+    dsaidx_k_args k;
+    memset(&rope, 0, sizeof rope);
+    memset(&q, 0, sizeof q);
+    memset(&k, 0, sizeof k);
+    if (dsaidx_abi_version() != DSAIDX_ABI_VERSION) return 1;
+    if (dsaidx_struct_size(0) != sizeof(dsaidx_rope)) return 2;
+    if (dsaidx_struct_size(1) != sizeof(dsaidx_q_args)) return 3;
+    if (dsaidx_struct_size(2) != sizeof(dsaidx_k_args)) return 4;
+    /* empty calls: OK without touching a device */
+    if (dsaidx_qk_fused(&q, &k, &rope, NULL) != DSAIDX_OK) return 5;
+    if (dsaidx_topk_per_row(NULL, 0, NULL, 0, 0, 1, NULL, NULL, 0, NULL) != DSAIDX_OK) return 6;
+    /* rejected on the host */
+    q.num_tokens = 1;
+    if (dsaidx_q_rope_quant_fold(&q, &rope, NULL) != DSAIDX_ERR_INVALID_ARGUMENT) return 7;
+    if (dsaidx_topk_workspace_bytes(1, 1 << 20, 2048) <= 0) return 8;
+    printf("%s %d\n", dsaidx_status_string(DSAIDX_ERR_UNSUPPORTED), dsaidx_device_supported(-1));
+    return 0;
+}
+"""
+
+
+def test_header_compiles_and_links_as_c99(L, tmp_path):
+    """include/dsaidx.h is plain C: a C99 program built with -Wall -Werror
+    against it links to libdsaidx.so and runs the host-side paths."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "abi.c"
+    exe = tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", HEADER_DIR,
+                    str(src), "-o", str(exe), "-L", libdir, "-ldsaidx", "-Wl,-rpath," + libdir],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == "DSAIDX_ERR_UNSUPPORTED 0"
