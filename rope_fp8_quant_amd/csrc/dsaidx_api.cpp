@@ -103,7 +103,10 @@ void fill_q(PrepParams& p, const dsaidx_q_args& q) {
     p.q_scale = q.q_scale_out;
     p.weight_scale = q.weight_scale;
     p.H = q.num_heads;
-    p.head_blocks = (q.num_heads + dsaidx::kHeadsPerItem - 1) / dsaidx::kHeadsPerItem;
+    p.heads_per_item = q.num_tokens * q.num_heads <= dsaidx::kSmallBatchHeadRows
+                           ? dsaidx::kHeadsPerItemSmall
+                           : dsaidx::kHeadsPerItem;
+    p.head_blocks = (q.num_heads + p.heads_per_item - 1) / p.heads_per_item;
     p.q_items = q.num_tokens * p.head_blocks;
     p.T = q.num_tokens;
 }

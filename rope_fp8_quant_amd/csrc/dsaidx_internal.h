@@ -9,10 +9,12 @@ namespace dsaidx {
 constexpr int kRow = 128;           // elements per head vector / key row
 constexpr int kLanesPerRow = 16;    // one DPP row of a wavefront per vector
 constexpr int kRowsPerWave = 4;     // 64 lanes / 16
-#ifndef DSAIDX_HEADS_PER_ITEM
-#define DSAIDX_HEADS_PER_ITEM 16
-#endif
-constexpr int kHeadsPerItem = DSAIDX_HEADS_PER_ITEM;  // query heads per wavefront work item
+// Query heads per wavefront work item: 16 for large batches; 4 when the call
+// has at most kSmallBatchHeadRows query rows, where more, shorter work items
+// cut the latency of a call that cannot fill the GPU.
+constexpr int kHeadsPerItem = 16;
+constexpr int kHeadsPerItemSmall = 4;
+constexpr int64_t kSmallBatchHeadRows = 16384;
 constexpr int kTokensPerKItem = 4;  // key rows per wavefront work item
 constexpr int32_t kKeyBf16Intermediate = 0x1;  // DSAIDX_K_BF16_INTERMEDIATE
 constexpr int32_t kKeyPagedCache = 0x2;        // DSAIDX_K_PAGED_CACHE
@@ -22,7 +24,7 @@ constexpr int kPagedScaleBytes = 4;            // fp32 scale per slot in a paged
 // the others query work items (which ones: see the kernel); either set may be
 // empty.
 struct PrepParams {
-    // query rows: item = (token, block of 16 heads)
+    // query rows: item = (token, block of heads_per_item heads)
     const uint16_t* q;
     int64_t q_st, q_sh;
     const uint16_t* w;
@@ -33,7 +35,8 @@ struct PrepParams {
     float* q_scale;
     float weight_scale;
     int32_t H;
-    int32_t head_blocks;  // ceil(H / 16)
+    int32_t heads_per_item;  // kHeadsPerItem or kHeadsPerItemSmall
+    int32_t head_blocks;  // ceil(H / heads_per_item)
     int32_t k_blocks;
     int64_t q_items;      // T * head_blocks (0 when the dispatch has no query work)
     // key rows: item = 4 consecutive tokens

@@ -20,10 +20,14 @@
 //   contig lane j holds [8j, 8j+8); used for NeoX with rope_dim 80..128.
 // Row reductions (max |y|, LayerNorm sums) are four DPP row_ror steps; the
 // NeoX partner values come from ds_bpermute.  A query work item is one token
-// and 16 heads (4 passes of 4 vectors): the token's cos/sin sit in registers
-// for all 16 heads, and the 16 folded head gates of the item are produced by
-// one coalesced load and store.  A key work item is 4 tokens.  Key and query
-// work items share one dispatch: the last k_blocks workgroups take key items.
+// and HPI heads (HPI / 4 passes of 4 vectors): the token's cos/sin sit in
+// registers for all of them, and the item's HPI folded head gates are produced
+// by one coalesced load and store.  HPI is 16, or 4 for calls of at most 16384
+// query rows: a small batch cannot fill the GPU, and more, shorter items cut
+// its latency (64 tokens x 64 heads: 2.6 us against 3.0 us per call), while
+// for large batches 16-head items move fewer cos/sin rows and gates per byte
+// of q.  A key work item is 4 tokens.  Key and query work items share one
+// dispatch: the last k_blocks workgroups take key items.
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
 // is rounded on its own (contraction is off), the LayerNorm sums are fp64, and
@@ -55,7 +59,6 @@
 namespace dsaidx {
 namespace {
 
-constexpr int kPasses = kHeadsPerItem / kRowsPerWave;
 constexpr int kContig = 0;
 constexpr int kSplit = 1;
 
@@ -382,8 +385,9 @@ __device__ __forceinline__ void rope_packed_row(const uint4& raw, float x[8], co
 
 // ---------------------------------------------------------- work items ----
 
-template <int STYLE, int LAYOUT>
+template <int STYLE, int LAYOUT, int HPI>
 __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, int lane) {
+    constexpr int kPasses = HPI / kRowsPerWave;
     const int g = lane >> 4;
     const int j = lane & (kLanesPerRow - 1);
     const int64_t t = item / p.head_blocks;
@@ -391,15 +395,15 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
     const int64_t pos = clamp_position(p.q_pos[t], p.P);
     const RopeLane rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
     // Head of this row group in pass ps: h0 + 4 * ps.
-    const int hbase = hb * kHeadsPerItem;
+    const int hbase = hb * HPI;
     const int h0 = hbase + g;
     const uint16_t* src = p.q + t * p.q_st + (int64_t)h0 * p.q_sh;
     const int64_t src_pass = (int64_t)kRowsPerWave * p.q_sh;
     uint8_t* dst = p.q_fp8 + (t * p.H + h0) * kRow;
 
-    // Every load of the item first: the rows, and the 16 head gates (lane l
+    // Every load of the item first: the rows, and the HPI head gates (lane l
     // of the first row group takes head hbase + l).
-    const bool gate_lane = lane < kHeadsPerItem && hbase + lane < p.H;
+    const bool gate_lane = lane < HPI && hbase + lane < p.H;
     uint32_t wbits = 0;
     if (gate_lane) wbits = p.w[t * p.w_st + hbase + lane];
     uint4 raw[kPasses];
@@ -513,7 +517,7 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
     }
 }
 
-template <int STYLE, int LAYOUT>
+template <int STYLE, int LAYOUT, int HPI>
 __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -539,7 +543,7 @@ __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     } else {
         const int64_t stride = nq * waves;
         for (int64_t it = qb * waves + wave; it < p.q_items; it += stride)
-            query_item<STYLE, LAYOUT>(p, it, lane);
+            query_item<STYLE, LAYOUT, HPI>(p, it, lane);
     }
 }
 
@@ -575,13 +579,17 @@ hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned b
                        hipStream_t stream) {
     PrepParams copy = p;
     void* args[] = {&copy};
+    const bool small = p.heads_per_item == kHeadsPerItemSmall;
     const void* fn;
     if (style == 1)
-        fn = reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1, kSplit>);
+        fn = small ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall>)
+                   : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem>);
     else if (p.R <= 64)
-        fn = reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kSplit>);
+        fn = small ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall>)
+                   : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem>);
     else
-        fn = reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kContig>);
+        fn = small ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall>)
+                   : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItem>);
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream);
 }
 
