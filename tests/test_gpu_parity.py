@@ -495,3 +495,48 @@ def test_offsets_beyond_2_pow_31_elements():
     assert np.all(k_cache[T:].cpu().numpy() == SENTINEL)
     log("fused T=270000 (offsets > 2^31)", dict(tokens_checked=int(len(tokens)),
                                                  k_bytes_differ=int(np.count_nonzero(d))))
+
+
+# ------------------------------------------------ randomized combinations ----
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_combinations(seed):
+    """Seeded random draws across the argument space at once: token and head
+    counts (both item sizes), rope_dim and style, value recipe, padded head
+    stride, the projection-output layout, a combined table, cache row padding,
+    both cache layouts and writers, weight_scale and every entry point."""
+    rng = np.random.default_rng(5000 + seed)
+    if seed % 2:        # above 16384 query rows: 16-head work items
+        T = int(rng.choice([700, 1500]))
+        H = int(rng.choice([33, 64, 80]))
+    else:
+        T = int(rng.choice([1, 3, 41, 64, 130, 255, 256, 257, 700]))
+        H = int(rng.choice([1, 4, 7, 16, 33, 64, 80]))
+    rope_dim = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    style = int(rng.choice([W.NEOX, W.INTERLEAVED]))
+    values = str(rng.choice(["normal", "student_t3", "outlier_channels", "sparse_outliers",
+                             "zero_rows"]))
+    flags = int(rng.choice([0, R.DSAIDX_K_BF16_INTERMEDIATE, R.DSAIDX_K_PAGED_CACHE,
+                            R.DSAIDX_K_PAGED_CACHE | R.DSAIDX_K_BF16_INTERMEDIATE]))
+    page = int(rng.choice([2, 16, 64])) if flags & R.DSAIDX_K_PAGED_CACHE else 0
+    entry = str(rng.choice(["fused", "q+k", "q", "k", "k_only"]))
+    pad_row = 0 if flags & R.DSAIDX_K_PAGED_CACHE else int(rng.choice([0, 8, 64]))
+    wl = W.make(T, H, rope_dim=rope_dim, style=style, values=values, table_rows=4096,
+                num_slots=4096, seed=seed, name="random%d" % seed)
+    wl.weight_scale = float(rng.choice([1.0, 0.5, 0.0883883461356163]))
+    c = DeviceCase(wl, q_head_pad=int(rng.choice([0, 8])), gemm_layout=bool(rng.integers(2)),
+                   combined_table=bool(rng.integers(2)), cache_row_pad=pad_row,
+                   q_scale_out=bool(rng.integers(2)), k_flags=flags, page_size=page)
+    c.run(entry)
+    out = c.host()
+    rep = dict(T=T, H=H, rope_dim=rope_dim, style=style, values=values, flags=flags, page=page,
+               entry=entry)
+    if entry != "k" and entry != "k_only":
+        check_q(out, wl, rep)
+    else:
+        assert np.all(out["q_fp8"] == SENTINEL)
+    if entry != "q":
+        check_k(out, wl, rep, cache_row_pad=pad_row, k_flags=flags, page_size=page)
+    else:
+        assert np.all(out["k_cache"] == SENTINEL)
+    log("random %d" % seed, rep)

@@ -282,3 +282,28 @@ def test_long_rows_threshold_bin_over_list_capacity():
     lens = np.array([cols, cols - 7, 60001, 40000], np.int32)
     out = run_topk(x, k, lens)
     check(out, x, k, lens)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Seeded random draws over rows, columns, k, lengths, row padding and
+    value mixes, across the row kernel's shapes and the split-row path."""
+    rng = np.random.default_rng(7000 + seed)
+    cols = int(rng.choice([1, 100, 2049, 4096, 5000, 8192, 12345, 16384, 20000, 32768, 33000,
+                           70000]))
+    rows = int(rng.integers(1, max(2, min(40, 2_000_000 // max(cols, 1)))))
+    k = int(rng.choice([1, 7, 64, 2048, max(1, cols // 2), cols + 3]))
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    mix = int(rng.integers(4))
+    if mix == 1:
+        x = np.round(x * 4) / 4                                  # heavy ties
+    elif mix == 2:
+        x[rng.random((rows, cols)) < 0.05] = -np.inf             # masked keys
+        x[rng.random((rows, cols)) < 0.001] = np.inf
+    elif mix == 3:
+        x = (100.0 + 1e-3 * x).astype(np.float32)                # narrow range
+    lengths = None
+    if rng.integers(2):
+        lengths = rng.integers(-2, cols + 3, rows).astype(np.int32)
+    out = run_topk(x, k, lengths, pad_cols=int(rng.choice([0, 1, 7])))
+    check(out, x, k, lengths)
