@@ -264,9 +264,13 @@ def main():
 
         ms_eager = time_calls(torch, fused1, 2000, 200, WARM_MS_LATENCY)
         ms_graph = time_graph(torch, fused1, 100, 20)
+        # the floor for any dispatch under graph replay: a one-element fill
+        tiny = torch.zeros(1, dtype=torch.float32, device="cuda")
+        ms_floor = time_graph(torch, lambda: tiny.fill_(1.0), 100, 20)
         extras["decode_batch_T64"] = {"us_per_call_eager": ms_eager * 1e3,
                                       "us_per_call_graph": ms_graph * 1e3,
-                                      "bytes_per_call": W.bytes_per_call(64)}
+                                      "bytes_per_call": W.bytes_per_call(64),
+                                      "us_per_dispatch_floor_graph": ms_floor * 1e3}
         # 512-token decode, interleaved RoPE: fused and k-only
         wl2 = W.named(2)
         c2 = Case(wl2, torch, R)
