@@ -392,25 +392,43 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
     const int j = lane & (kLanesPerRow - 1);
     const int64_t t = item / p.head_blocks;
     const int hb = (int)(item - t * p.head_blocks);
-    const int64_t pos = clamp_position(p.q_pos[t], p.P);
-    const RopeLane rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
     // Head of this row group in pass ps: h0 + 4 * ps.
     const int hbase = hb * HPI;
     const int h0 = hbase + g;
-    const uint16_t* src = p.q + t * p.q_st + (int64_t)h0 * p.q_sh;
-    const int64_t src_pass = (int64_t)kRowsPerWave * p.q_sh;
     uint8_t* dst = p.q_fp8 + (t * p.H + h0) * kRow;
 
-    // Every load of the item first: the rows, and the HPI head gates (lane l
-    // of the first row group takes head hbase + l).
+    // Every load of the item before any arithmetic: the rows, the HPI head
+    // gates (lane l of the first row group takes head hbase + l), the
+    // position and the cos/sin row it selects.  Loads return in issue order.
+    // A multi-pass item fetches the position and cos/sin first, so pass 0 can
+    // start while the later rows are still arriving.  A one-pass item has
+    // nothing to overlap: it issues its row and gate first, unconditionally
+    // (heads past H clamped to H - 1: computed, never stored), so they travel
+    // while the position and then the cos/sin row come back -- two dependent
+    // round trips instead of three (3-10 % faster on batches of 41-256; the
+    // same order on multi-pass items measured 1-9 % slower on large batches).
+    const uint16_t* qt = p.q + t * p.q_st;
     const bool gate_lane = lane < HPI && hbase + lane < p.H;
-    uint32_t wbits = 0;
-    if (gate_lane) wbits = p.w[t * p.w_st + hbase + lane];
     uint4 raw[kPasses];
+    uint32_t wbits = 0;
+    int64_t pos;
+    RopeLane rl;
+    if (kPasses == 1) {
+        raw[0] = load_row<LAYOUT>(qt + (int64_t)min(h0, p.H - 1) * p.q_sh, j);
+        wbits = p.w[t * p.w_st + min(hbase + (lane < HPI ? lane : 0), p.H - 1)];
+        pos = clamp_position(p.q_pos[t], p.P);
+        rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
+    } else {
+        pos = clamp_position(p.q_pos[t], p.P);
+        rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
+        if (gate_lane) wbits = p.w[t * p.w_st + hbase + lane];
+        const uint16_t* src = qt + (int64_t)h0 * p.q_sh;
+        const int64_t src_pass = (int64_t)kRowsPerWave * p.q_sh;
 #pragma unroll
-    for (int ps = 0; ps < kPasses; ++ps) {
-        raw[ps] = make_uint4(0, 0, 0, 0);
-        if (h0 + ps * kRowsPerWave < p.H) raw[ps] = load_row<LAYOUT>(src + ps * src_pass, j);
+        for (int ps = 0; ps < kPasses; ++ps) {
+            raw[ps] = make_uint4(0, 0, 0, 0);
+            if (h0 + ps * kRowsPerWave < p.H) raw[ps] = load_row<LAYOUT>(src + ps * src_pass, j);
+        }
     }
 
     int e[kPasses];
