@@ -401,7 +401,9 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
     // gates (lane l of the first row group takes head hbase + l), the
     // position and the cos/sin row it selects.  Loads return in issue order.
     // A multi-pass item fetches the position and cos/sin first, so pass 0 can
-    // start while the later rows are still arriving.  A one-pass item has
+    // start while the later rows are still arriving, and its gates last: a
+    // conditional gate load ahead of the rows held them back until it
+    // returned (11 % on a 512-token call).  A one-pass item has
     // nothing to overlap: it issues its row and gate first, unconditionally
     // (heads past H clamped to H - 1: computed, never stored), so they travel
     // while the position and then the cos/sin row come back -- two dependent
@@ -421,7 +423,6 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
     } else {
         pos = clamp_position(p.q_pos[t], p.P);
         rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
-        if (gate_lane) wbits = p.w[t * p.w_st + hbase + lane];
         const uint16_t* src = qt + (int64_t)h0 * p.q_sh;
         const int64_t src_pass = (int64_t)kRowsPerWave * p.q_sh;
 #pragma unroll
@@ -429,6 +430,7 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
             raw[ps] = make_uint4(0, 0, 0, 0);
             if (h0 + ps * kRowsPerWave < p.H) raw[ps] = load_row<LAYOUT>(src + ps * src_pass, j);
         }
+        if (gate_lane) wbits = p.w[t * p.w_st + hbase + lane];
     }
 
     int e[kPasses];
