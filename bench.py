@@ -186,6 +186,29 @@ def cpu_baseline(wl, target_s=5.0, min_wall_s=1.2):
                        "threads" % (n, wl.T, wl.name, passes, total, cores))
 
 
+def topk_measurements(torch, R, W, steps=50):
+    """Top-k per row over index logits (index_topk = 2048) on the named
+    synthetic workloads: microseconds per call and algorithmic GB/s."""
+    out = {}
+    for ti in range(len(W.TOPK_NAMED)):
+        tw = W.topk_named(ti)
+        lg = torch.from_numpy(tw.logits).cuda()
+        ln = torch.from_numpy(tw.lengths).cuda()
+        rows, cols = tw.logits.shape
+        ot = torch.empty((rows, tw.k), dtype=torch.int32, device="cuda")
+        nws = R.dsaidx_topk_workspace_bytes(rows, cols, tw.k)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+        mst = time_calls(torch, lambda: R.dsaidx_topk_per_row(lg, tw.k, ot, ln, workspace=ws),
+                         steps, 5, WARM_MS)
+        bt = W.topk_bytes_per_call(rows, tw.lengths, tw.k)
+        out[tw.name] = {"us_per_call": mst * 1e3, "algorithmic_bytes": bt,
+                        "achieved_GBps": bt / (mst * 1e-3) / 1e9,
+                        "dispatches": 4 if nws else 1, "workspace_bytes": nws}
+        del lg, ln, ot, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +217,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode, prefill-chunk and k-only measurements")
+    ap.add_argument("--topk-only", action="store_true",
+                    help="time only the top-k-per-row workloads (a JSON object of its own)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -210,6 +235,9 @@ def main():
     torch.cuda.set_device(0)
     if not R.dsaidx_device_supported(0):
         raise SystemExit("cuda:0 is not a gfx950 device")
+    if args.topk_only:
+        print(json.dumps({"topk_per_row": topk_measurements(torch, R, W, args.steps)}), flush=True)
+        return
 
     log("generating long_prefill_T65536 inputs")
     wl = W.named(4)
@@ -308,23 +336,7 @@ def main():
                                          "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
         del sets
         torch.cuda.empty_cache()
-        # top-k per row over index logits (index_topk = 2048)
-        for ti in range(len(W.TOPK_NAMED)):
-            tw = W.topk_named(ti)
-            lg = torch.from_numpy(tw.logits).cuda()
-            ln = torch.from_numpy(tw.lengths).cuda()
-            rows, cols = tw.logits.shape
-            ot = torch.empty((rows, tw.k), dtype=torch.int32, device="cuda")
-            nws = R.dsaidx_topk_workspace_bytes(rows, cols, tw.k)
-            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
-            mst = time_calls(torch, lambda: R.dsaidx_topk_per_row(lg, tw.k, ot, ln, workspace=ws),
-                             50, 5, WARM_MS)
-            bt = W.topk_bytes_per_call(rows, tw.lengths, tw.k)
-            extras[tw.name] = {"us_per_call": mst * 1e3, "algorithmic_bytes": bt,
-                               "achieved_GBps": bt / (mst * 1e-3) / 1e9,
-                               "dispatches": 4 if nws else 1, "workspace_bytes": nws}
-            del lg, ln, ot, ws
-        torch.cuda.empty_cache()
+        extras.update(topk_measurements(torch, R, W))
         result["secondary"] = extras
 
     # plain device copy of the same byte count: the reference for achievable
