@@ -40,7 +40,7 @@ constexpr int kBins = 2048;
 
 __device__ __forceinline__ uint32_t order_key(float v) {
     const uint32_t u = __float_as_uint(v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 
@@ -205,7 +205,12 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     };
 
     // ---- load, as order keys; key 0 marks a slot outside the row (no logit
-    // that is not NaN has key 0)
+    // that is not NaN has key 0), so the count and write passes below need
+    // no bound checks.  Register group j (slots 4j..4j+3 of every thread) is
+    // full when all its slots lie inside the row, the same for the whole
+    // workgroup: only the group that straddles the row's end pays for
+    // per-slot checks.
+    auto full = [&](int j) -> bool { return (j + 1) * T * 4 <= n; };
     uint32_t key[V];
     {
         const float4* s4 = reinterpret_cast<const float4*>(src);
@@ -213,11 +218,20 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         for (int j = 0; j < V / 4; ++j) {
             const int32_t c = tid + j * T;
             float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live(4 * j) && 4 * c < n) f = s4[c];
-            key[4 * j + 0] = 4 * c + 0 < n ? order_key(f.x) : 0u;
-            key[4 * j + 1] = 4 * c + 1 < n ? order_key(f.y) : 0u;
-            key[4 * j + 2] = 4 * c + 2 < n ? order_key(f.z) : 0u;
-            key[4 * j + 3] = 4 * c + 3 < n ? order_key(f.w) : 0u;
+            if (full(j) || (live(4 * j) && 4 * c < n)) f = s4[c];
+            key[4 * j + 0] = order_key(f.x);
+            key[4 * j + 1] = order_key(f.y);
+            key[4 * j + 2] = order_key(f.z);
+            key[4 * j + 3] = order_key(f.w);
+        }
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) {
+            if (!full(j)) {
+                const int32_t c = tid + j * T;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!live(4 * j) || 4 * c + e >= n) key[4 * j + e] = 0u;
+            }
         }
     }
 
@@ -232,43 +246,69 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     // ---- 1. histogram of the keys' top 11 bits (slots outside the row count
     // in a spare bin of their lane) and the bin B1 of the k-th largest
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-        if (live(i)) atomicAdd(&hist0[key[i] ? key[i] >> 21 : (uint32_t)(kBins + lane)], 1u);
+    for (int j = 0; j < V / 4; ++j) {
+        if (full(j)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&hist0[key[4 * j + e] >> 21], 1u);
+        } else if (live(4 * j)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t kk = key[4 * j + e];
+                atomicAdd(&hist0[kk ? kk >> 21 : (uint32_t)(kBins + lane)], 1u);
+            }
+        }
+    }
     __syncthreads();
     uint32_t b1, rem;
     select_bin<T>(hist0, (uint32_t)k, part, sel, b1, rem);
     b1 = min(b1, (uint32_t)(kBins - 1));
     const uint32_t n1 = hist0[b1];           // logits in B1
     const uint32_t rem0 = rem;
-    const uint32_t key_hi = (b1 + 1) << 21;  // keys at or above are above B1 (0 when b1 is the top bin)
-    const uint32_t key_lo = b1 << 21;
-    auto above_b1 = [&](uint32_t kk) { return b1 < kBins - 1 && kk >= key_hi; };
-    auto in_b1 = [&](uint32_t kk) { return kk >= key_lo && (b1 == kBins - 1 || kk < key_hi) && kk; };
+    // Keys above hi_m1 are in bins above B1 (none when B1 is the top bin);
+    // keys above lo_m1 are in B1 or above.  Key 0 is above neither: B1 is
+    // never bin 0, which holds no logit that is not NaN.
+    const uint32_t hi_m1 = ((b1 + 1) << 21) - 1u;
+    const uint32_t lo_m1 = (b1 << 21) - 1u;
     auto bin_at = [&](int i) -> uint32_t { return key[i] >> 21; };
 
-    // ---- 2. bins above B1 go out at once; B1 goes to the LDS list
-    uint32_t n_gt = 0;
+    // ---- 2. bins above B1 go out at once and B1 goes to the LDS list, at
+    // offsets from one workgroup prefix sum of both counts (above B1 in the
+    // low half-word, in B1 in the high one; each total is at most 32768)
+    const bool listed = n1 <= (uint32_t)kCand;
+    {
+        uint32_t n_gt = 0, n_ge = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        if (live(i)) {
-            n_gt += above_b1(key[i]) ? 1u : 0u;
-            if (n1 <= (uint32_t)kCand && in_b1(key[i])) {
-                const uint32_t c = atomicAdd(&cnt[0], 1u);
-                if (c < (uint32_t)kCand) {
-                    cand_key[c] = key[i];
-                    cand_pos[c] = pos(i);
+        for (int i = 0; i < V; ++i) {
+            n_gt += key[i] > hi_m1 ? 1u : 0u;
+            n_ge += key[i] > lo_m1 ? 1u : 0u;
+        }
+        const uint32_t packed = n_gt | ((n_ge - n_gt) << 16);
+        const uint32_t before = block_inclusive_sum<T>(packed, part) - packed;
+        // Compare again below rather than keep 2V lane masks alive across the
+        // prefix sum (they would spill to VGPR lanes).
+#pragma unroll
+        for (int i = 0; i < V; ++i) asm volatile("" : "+v"(key[i]));
+        uint32_t o_gt = before & 0xFFFFu;
+        if (listed) {
+            uint32_t o_b1 = before >> 16;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if (key[i] > hi_m1) {
+                    dst[o_gt++] = pos(i);
+                } else if (key[i] > lo_m1) {
+                    cand_key[o_b1] = key[i];
+                    cand_pos[o_b1] = pos(i);
+                    ++o_b1;
                 }
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                if (key[i] > hi_m1) dst[o_gt++] = pos(i);
         }
     }
-    {
-        uint32_t o = block_inclusive_sum<T>(n_gt, part) - n_gt;
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-            if (live(i) && above_b1(key[i])) write(o++, pos(i));
-    }
     const uint32_t above0 = (uint32_t)k - rem0;  // slots taken by the bins above B1
-    const bool listed = n1 <= (uint32_t)kCand;
+    __syncthreads();                             // the list is complete
 
     // ---- 3a. a short list: one wavefront ranks it directly
     if (n1 <= 64) {
