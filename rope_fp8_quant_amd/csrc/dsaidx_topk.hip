@@ -17,14 +17,18 @@
 //   1. a 2048-bin histogram of the keys' top 11 bits (sign, exponent, two
 //      mantissa bits); a scan from the top finds the bin B1 holding the k-th
 //      largest logit and its rank in B1;
-//   2. logits in bins above B1 are written at slots given by one workgroup
-//      prefix sum (no atomics); B1's logits go to an LDS list;
-//   3. a list of at most 64 is ranked by one wavefront directly; a longer one
-//      is radix-selected on keys relative to its smallest key (11-bit digits,
-//      most often one or two passes, none for a tie group), over the list or,
-//      when B1 overflows it (a narrow value range), over the registers; then
-//      the list's keys above the k-th and the needed keys equal to it fill
-//      the remaining slots.
+//   2. logits in bins above B1 are written, and B1's logits appended to an
+//      LDS list, at offsets from one workgroup prefix sum of both counts (no
+//      atomics);
+//   3. a list of at most 64 is ranked by one wavefront directly.  A longer
+//      one is radix-selected on 11-bit digits: in calls of many rows by one
+//      wavefront alone, on the 21 bits below B1's prefix (two passes, no
+//      workgroup barriers, the other wavefronts leave the compute unit to
+//      other rows); in smaller calls by the whole workgroup, on keys relative
+//      to the list's smallest key (most often one or two passes, none for a
+//      tie group).  When B1 overflows the list (a narrow value range), the
+//      workgroup selects over the registers.  The list's keys above the k-th
+//      and the needed keys equal to it fill the remaining slots.
 // Linear bins between the row's min and max adapt better to a narrow value
 // range, but cost a min/max pass and about eight more instructions per logit:
 // 14.5 against 12.5 us for 64 rows of 16384, 75 against 72 us for the causal
@@ -152,6 +156,50 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, uint32_t want, 
     select_bin_regs<T>(h, want, part, sel, bin, rank);
 }
 
+// Lanes of this wavefront below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Orders this wavefront's earlier LDS writes and atomics before its later LDS
+// reads by other lanes (a wavefront's LDS operations complete in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wavefront, every lane active: the bin of an NB-bin LDS histogram
+// (ranked from the top) that holds the element of rank `want` (1-based, at
+// most the histogram's total), and that element's rank inside the bin.
+// Lane l sums the NB/64 bins below NB - l*NB/64; a wavefront scan finds the
+// lane whose bins hold rank `want`, then the first NB/64 lanes scan that
+// lane's bins one each.
+template <int NB>
+__device__ __forceinline__ void wave_select(const uint32_t* h, uint32_t want, uint32_t& bin,
+                                            uint32_t& rank) {
+    constexpr int PL = NB / 64;
+    static_assert(PL % 4 == 0 && PL <= 64, "bins per lane");
+    const int lane = threadIdx.x & 63;
+    uint32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < PL; q += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&h[NB - (lane + 1) * PL + q]);
+        s += v.x + v.y + v.z + v.w;
+    }
+    const uint32_t incl = wave_inclusive_sum(s);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(incl >= want);
+    const int L = m ? (int)__builtin_ctzll(m) : 63;
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - s), L);
+    const int top = NB - 1 - L * PL;                      // lane L's highest bin
+    const uint32_t c = lane < PL ? h[top - lane] : 0u;
+    const uint32_t ci = wave_inclusive_sum(c);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < PL && above + ci >= want);
+    const int j = m2 ? (int)__builtin_ctzll(m2) : PL - 1;
+    bin = (uint32_t)(top - j);
+    rank = want - above - (uint32_t)__builtin_amdgcn_readlane((int)(ci - c), j);
+}
+
 struct RowArgs {
     const float* logits;
     int64_t row_stride;
@@ -159,6 +207,7 @@ struct RowArgs {
     int64_t cols;
     int32_t k;
     int32_t* out;            // [rows, k]
+    int32_t solo;            // nonzero: wavefront 0 alone resolves a listed B1
 };
 
 constexpr int kCand = 1024;   // B1 logits kept in an LDS list (more: they stay in registers)
@@ -169,8 +218,8 @@ template <int T, int V, int MINW>
 __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     static_assert(V % 4 == 0 && V <= 32, "V");
     constexpr int W = T / 64;
-    __shared__ uint32_t hist0[kBins + 64];   // coarse bins, then radix digits; 64 spare bins
-    __shared__ uint32_t hist1[kBins];        // radix digits
+    __shared__ __align__(16) uint32_t hist0[kBins + 64];   // coarse bins, then radix digits; 64 spare bins
+    __shared__ __align__(16) uint32_t hist1[kBins];        // radix digits
     __shared__ uint32_t cand_key[kCand];
     __shared__ int32_t cand_pos[kCand];
     __shared__ uint32_t part[W];
@@ -235,8 +284,15 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         }
     }
 
-    for (int b = tid; b < kBins + 64; b += T) hist0[b] = 0;
-    for (int b = tid; b < kBins; b += T) hist1[b] = 0;
+    {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int b = 4 * tid; b < kBins; b += 4 * T) {
+            *reinterpret_cast<uint4*>(&hist0[b]) = z;
+            *reinterpret_cast<uint4*>(&hist1[b]) = z;
+        }
+        if (tid < 16) *reinterpret_cast<uint4*>(&hist0[kBins + 4 * tid]) = z;
+    }
     if (tid < 3) cnt[tid] = 0;
     if (tid == 0) {
         sel[0] = 0;
@@ -310,7 +366,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     const uint32_t above0 = (uint32_t)k - rem0;  // slots taken by the bins above B1
     __syncthreads();                             // the list is complete
 
-    // ---- 3a. a short list: one wavefront ranks it directly
+    // ---- 3a. a short list: wavefront 0 ranks it directly
     if (n1 <= 64) {
         if (wave == 0) {
             const bool mine = (uint32_t)lane < n1;
@@ -325,8 +381,58 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         return;
     }
 
-    // ---- 3b. exact rank-`rem` key inside B1 by radix select, over the list
-    // or, when B1 overflows it, over the registers
+    // ---- 3b. a longer list, when many rows share each compute unit:
+    // wavefront 0 alone resolves it with no further workgroup barriers, and
+    // the other wavefronts leave the compute unit to other rows.  B1's keys
+    // share their top 11 bits; two radix passes on the 21 bits below (11,
+    // then 10) give the rank-rem0 key.  Bin indices are masked so that they
+    // stay inside the histograms whatever the list holds.
+    if (listed && a.solo) {
+        if (wave != 0) return;
+        const uint32_t base = b1 << 21;
+        for (uint32_t c = lane; c < n1; c += 64)
+            atomicAdd(&hist1[((cand_key[c] - base) >> 10) & (kBins - 1)], 1u);
+        {
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int b = 4 * lane; b < 1024; b += 4 * 64) *reinterpret_cast<uint4*>(&hist0[b]) = z;
+        }
+        wave_lds_sync();
+        uint32_t d1, r1;
+        wave_select<kBins>(hist1, rem0, d1, r1);
+        for (uint32_t c = lane; c < n1; c += 64) {
+            const uint32_t rk = cand_key[c] - base;
+            if (((rk >> 10) & (kBins - 1)) == d1) atomicAdd(&hist0[rk & 1023u], 1u);
+        }
+        wave_lds_sync();
+        uint32_t d2, r2;
+        wave_select<1024>(hist0, r1, d2, r2);
+        const uint32_t kth = base + (d1 << 10) + d2;
+        // keys above kth fill [above0, k - r2); the first r2 keys equal to it
+        // fill [k - r2, k)
+        uint32_t n_above = 0, n_eq = 0;
+        for (uint32_t c0 = 0; c0 < n1; c0 += 64) {
+            const uint32_t c = c0 + lane;
+            const bool ok = c < n1;
+            const uint32_t key = ok ? cand_key[c] : 0u;
+            const bool gt = ok && key > kth;
+            const bool eq = ok && key == kth;
+            const uint64_t mg = __builtin_amdgcn_ballot_w64(gt);
+            const uint64_t me = __builtin_amdgcn_ballot_w64(eq);
+            if (gt) write(above0 + n_above + lanes_below(mg), cand_pos[c]);
+            if (eq) {
+                const uint32_t q = n_eq + lanes_below(me);
+                if (q < r2) write((uint32_t)k - r2 + q, cand_pos[c]);
+            }
+            n_above += (uint32_t)__builtin_popcountll(mg);
+            n_eq += (uint32_t)__builtin_popcountll(me);
+        }
+        return;
+    }
+
+    // ---- 4. otherwise every wavefront takes part in a radix select for the
+    // exact rank-`rem` key inside B1, over the list or, when B1 overflows it
+    // (a narrow value range), over the registers
     auto for_b1 = [&](auto f) {
         if (listed) {
             for (uint32_t c = tid; c < n1; c += T) f(cand_key[c], cand_pos[c]);
@@ -380,7 +486,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     }
     const uint32_t kth = kmin + pfx;
 
-    // ---- 4. B1 outputs: keys above kth fill [above0, k - rem), then `rem`
+    // ---- 5. B1 outputs: keys above kth fill [above0, k - rem), then `rem`
     // keys equal to kth fill [k - rem, k)
     const uint32_t above = (uint32_t)k - rem;
     for_b1([&](uint32_t key, int32_t p) {
@@ -679,6 +785,11 @@ struct TopkPlan {
 #define DSAIDX_TOPK_R16K 1024, 16, 1
 #define DSAIDX_TOPK_R32K 1024, 32, 1
 constexpr int64_t kRowMax = 32768;       // longest row of the row kernel
+// From this many rows (several row workgroups per compute unit) a long B1
+// list is resolved by one wavefront, which frees the compute unit for other
+// rows sooner; with fewer rows compute units idle, and every wavefront of the
+// row's workgroup shares that work to shorten the row's latency.
+constexpr int64_t kSoloRows = 1024;
 
 static TopkPlan plan_topk(int64_t rows, int64_t cols, int32_t) {
     TopkPlan p{0, 0, 0, 0};
@@ -715,7 +826,7 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
                        hipStream_t stream) {
     const TopkPlan p = plan_topk(rows, cols, k);
     if (!p.split) {
-        RowArgs a{logits, row_stride, lengths, cols, k, out};
+        RowArgs a{logits, row_stride, lengths, cols, k, out, rows >= kSoloRows ? 1 : 0};
         switch (p.variant) {
             case 0: return launch_row<DSAIDX_TOPK_R4K>(a, rows, stream);
             case 1: return launch_row<DSAIDX_TOPK_R8K>(a, rows, stream);

@@ -108,6 +108,23 @@ def test_many_rows_prefill_shape():
     check(out, wl.logits, 512, wl.lengths)
 
 
+@pytest.mark.parametrize("cols", [3000, 8192, 12000, 30000])
+def test_list_paths_across_row_counts(cols):
+    """From 1024 rows on, a call resolves each long B1 list with one
+    wavefront; smaller calls use the whole workgroup.  The same rows go
+    through both: plain rows (lists of a few hundred), rows of heavy ties (a
+    B1 of one repeated value) and narrow-range rows (B1 beyond the list)."""
+    k = 2048
+    rng = np.random.default_rng(cols)
+    x = rng.standard_normal((1024, cols)).astype(np.float32)
+    x[1::3] = np.round(x[1::3] * 8) / 8
+    x[2::7] = (100.0 + 1e-3 * x[2::7]).astype(np.float32)
+    lengths = rng.integers(k - 10, cols + 1, 1024).astype(np.int32)
+    for rows in (1024, 1023):
+        out = run_topk(x[:rows], k, lengths[:rows])
+        check(out, x[:rows], k, lengths[:rows])
+
+
 def test_empty_and_invalid_calls():
     x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
     out = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
