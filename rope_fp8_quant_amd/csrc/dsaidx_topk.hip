@@ -430,17 +430,66 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         return;
     }
 
-    // ---- 4. otherwise every wavefront takes part in a radix select for the
-    // exact rank-`rem` key inside B1, over the list or, when B1 overflows it
-    // (a narrow value range), over the registers
-    auto for_b1 = [&](auto f) {
-        if (listed) {
-            for (uint32_t c = tid; c < n1; c += T) f(cand_key[c], cand_pos[c]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i)
-                if (live(i) && key[i] && bin_at(i) == b1) f(key[i], pos(i));
+    // ---- 4. a longer list in a smaller call: the same two radix passes, with
+    // every wavefront adding to the digit histograms and wavefront 0 choosing
+    // each digit (one barrier to publish it), then every wavefront writes
+    if (listed) {
+        const uint32_t base = b1 << 21;
+        for (uint32_t c = tid; c < n1; c += T)
+            atomicAdd(&hist1[((cand_key[c] - base) >> 10) & (kBins - 1)], 1u);
+        {
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            for (int b = 4 * tid; b < 1024; b += 4 * T) *reinterpret_cast<uint4*>(&hist0[b]) = z;
         }
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t d, r;
+            wave_select<kBins>(hist1, rem0, d, r);
+            if (lane == 0) {
+                sel[0] = d;
+                sel[1] = r;
+            }
+        }
+        __syncthreads();
+        const uint32_t d1 = sel[0], r1 = sel[1];
+        for (uint32_t c = tid; c < n1; c += T) {
+            const uint32_t rk = cand_key[c] - base;
+            if (((rk >> 10) & (kBins - 1)) == d1) atomicAdd(&hist0[rk & 1023u], 1u);
+        }
+        __syncthreads();                                     // also: every thread has read sel
+        if (wave == 0) {
+            uint32_t d, r;
+            wave_select<1024>(hist0, r1, d, r);
+            if (lane == 0) {
+                sel[0] = d;
+                sel[1] = r;
+            }
+        }
+        __syncthreads();
+        const uint32_t kth = base + (d1 << 10) + sel[0];
+        const uint32_t r2 = sel[1];
+        // keys above kth fill [above0, k - r2); r2 keys equal to it fill [k - r2, k)
+        for (uint32_t c = tid; c < n1; c += T) {
+            const uint32_t key = cand_key[c];
+            if (key > kth) {
+                write(above0 + atomicAdd(&cnt[1], 1u), cand_pos[c]);
+            } else if (key == kth) {
+                const uint32_t q = atomicAdd(&cnt[2], 1u);
+                if (q < r2) write((uint32_t)k - r2 + q, cand_pos[c]);
+            }
+        }
+        return;
+    }
+
+    // ---- 5. B1 overflowed the list (a narrow value range): every wavefront
+    // takes part in a radix select over the registers for the exact rank-`rem`
+    // key inside B1, on keys relative to B1's smallest key (its span decides
+    // the digits, so a narrow range spreads over the bins; none for a tie
+    // group)
+    auto for_b1 = [&](auto f) {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            if (live(i) && key[i] && bin_at(i) == b1) f(key[i], pos(i));
     };
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
     for_b1([&](uint32_t key, int32_t) {
@@ -472,6 +521,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         const int db = top < 11 ? top : 11;
         const int sh = top - db;
         uint32_t* h = (pass & 1) ? hist0 : hist1;
+        asm volatile("" : "+v"(kmin));   // keeps key - kmin inside the loop (no 2V-register hoist)
         for_b1([&](uint32_t key, int32_t) {
             const uint32_t rk = key - kmin;
             if (top >= 32 || (rk >> top) == pfx) atomicAdd(&h[(rk >> sh) & ((1u << db) - 1u)], 1u);
@@ -486,8 +536,8 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     }
     const uint32_t kth = kmin + pfx;
 
-    // ---- 5. B1 outputs: keys above kth fill [above0, k - rem), then `rem`
-    // keys equal to kth fill [k - rem, k)
+    // B1 outputs: keys above kth fill [above0, k - rem), then `rem` keys
+    // equal to kth fill [k - rem, k)
     const uint32_t above = (uint32_t)k - rem;
     for_b1([&](uint32_t key, int32_t p) {
         if (key > kth) {
