@@ -315,9 +315,17 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         }
     }
     __syncthreads();
-    uint32_t b1, rem;
-    select_bin<T>(hist0, (uint32_t)k, part, sel, b1, rem);
-    b1 = min(b1, (uint32_t)(kBins - 1));
+    if (wave == 0) {
+        uint32_t bin, rank;
+        wave_select<kBins>(hist0, (uint32_t)k, bin, rank);
+        if (lane == 0) {
+            sel[0] = bin;
+            sel[1] = rank;
+        }
+    }
+    __syncthreads();
+    const uint32_t b1 = sel[0];
+    uint32_t rem = sel[1];
     const uint32_t n1 = hist0[b1];           // logits in B1
     const uint32_t rem0 = rem;
     // Keys above hi_m1 are in bins above B1 (none when B1 is the top bin);
