@@ -179,12 +179,16 @@ template <int NB>
 __device__ __forceinline__ void wave_select(const uint32_t* h, uint32_t want, uint32_t& bin,
                                             uint32_t& rank) {
     constexpr int PL = NB / 64;
-    static_assert(PL % 4 == 0 && PL <= 64, "bins per lane");
+    static_assert(PL % 4 == 0 && PL <= 64 && (PL & (PL - 1)) == 0, "bins per lane");
     const int lane = threadIdx.x & 63;
+    // Each lane starts at another 16-byte piece of its bins, so that the
+    // lanes of one load spread over the LDS banks (lanes PL words apart would
+    // otherwise all hit the same banks).
     uint32_t s = 0;
 #pragma unroll
     for (int q = 0; q < PL; q += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&h[NB - (lane + 1) * PL + q]);
+        const int qs = (q + 4 * lane) & (PL - 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(&h[NB - (lane + 1) * PL + qs]);
         s += v.x + v.y + v.z + v.w;
     }
     const uint32_t incl = wave_inclusive_sum(s);
