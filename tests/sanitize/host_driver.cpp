@@ -1,0 +1,429 @@
+// Host-layer checks of libdsaidx under AddressSanitizer and
+// UndefinedBehaviorSanitizer, on the CPU.  dsaidx_api.cpp is linked against
+// stubs of the kernel launchers and of the two HIP device queries, which
+// record what the host layer asks for.  Pointers are real, aligned host
+// memory that nothing dereferences.  Exit status 0 when every check passes.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "dsaidx.h"
+#include "dsaidx_internal.h"
+
+namespace {
+
+struct Launch {
+    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test
+    dsaidx::PrepParams p;
+    int style;
+    unsigned grid, block;
+    int64_t rows, cols, row_stride, n;
+    int32_t k;
+    const void* workspace;
+};
+
+std::vector<Launch> g_launches;
+hipError_t g_fail = hipSuccess;  // what the launch stubs return
+int g_errors = 0;
+
+#define CHECK(c)                                                                   \
+    do {                                                                           \
+        if (!(c)) {                                                                \
+            std::fprintf(stderr, "FAILED %s:%d: %s\n", __FILE__, __LINE__, #c);    \
+            ++g_errors;                                                            \
+        }                                                                          \
+    } while (0)
+
+alignas(64) unsigned char g_arena[1 << 16];
+
+template <typename P>
+P* at(size_t off) { return reinterpret_cast<P*>(g_arena + off); }
+
+}  // namespace
+
+namespace dsaidx {
+
+hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned block, hipStream_t) {
+    Launch l;
+    std::memset(&l, 0, sizeof l);
+    l.kind = 0;
+    l.p = p;
+    l.style = style;
+    l.grid = grid;
+    l.block = block;
+    g_launches.push_back(l);
+    return g_fail;
+}
+
+hipError_t launch_topk(const float*, int64_t row_stride, const int32_t*, int64_t rows, int64_t cols,
+                       int32_t k, int32_t*, void* workspace, hipStream_t) {
+    Launch l;
+    std::memset(&l, 0, sizeof l);
+    l.kind = 1;
+    l.rows = rows;
+    l.cols = cols;
+    l.row_stride = row_stride;
+    l.k = k;
+    l.workspace = workspace;
+    g_launches.push_back(l);
+    return g_fail;
+}
+
+hipError_t launch_fp8_selftest(const float*, uint8_t*, int64_t n, unsigned grid, hipStream_t) {
+    Launch l;
+    std::memset(&l, 0, sizeof l);
+    l.kind = 2;
+    l.n = n;
+    l.grid = grid;
+    g_launches.push_back(l);
+    return g_fail;
+}
+
+// The size include/dsaidx.h documents.
+int64_t topk_workspace_bytes(int64_t rows, int64_t cols, int32_t) {
+    if (cols <= 32768) return 0;
+    if (rows * ((cols + 4095) / 4096) >= (int64_t(1) << 31)) return -1;
+    int64_t list = cols / 16 > 4096 ? cols / 16 : 4096;
+    list = (list + 3) / 4 * 4;
+    return rows * (16416 + 8 * list);
+}
+
+}  // namespace dsaidx
+
+extern "C" {
+hipError_t hipGetDeviceCount(int* count) {
+    *count = 0;
+    return hipErrorNoDevice;
+}
+hipError_t hipGetDeviceProperties(hipDeviceProp_t*, int) { return hipErrorNoDevice; }
+}
+
+namespace {
+
+dsaidx_rope make_rope() {
+    dsaidx_rope r;
+    std::memset(&r, 0, sizeof r);
+    r.cos = at<const float>(0);
+    r.sin = at<const float>(1024);
+    r.row_stride = 32;
+    r.max_position = 4096;
+    r.rope_dim = 64;
+    r.style = DSAIDX_ROPE_NEOX;
+    return r;
+}
+
+dsaidx_q_args make_q(int64_t T, int32_t H) {
+    dsaidx_q_args q;
+    std::memset(&q, 0, sizeof q);
+    q.q = at<const uint16_t>(2048);
+    q.q_stride_h = 128;
+    q.q_stride_t = 128 * (int64_t)H;
+    q.weights = at<const uint16_t>(4096);
+    q.w_stride_t = H;
+    q.positions = at<const int64_t>(6144);
+    q.num_tokens = T;
+    q.num_heads = H;
+    q.weight_scale = 1.0f;
+    q.q_fp8 = at<uint8_t>(8192);
+    q.weights_out = at<float>(10240);
+    q.q_scale_out = nullptr;
+    return q;
+}
+
+dsaidx_k_args make_k(int64_t T) {
+    dsaidx_k_args k;
+    std::memset(&k, 0, sizeof k);
+    k.k = at<const uint16_t>(12288);
+    k.k_stride_t = 128;
+    k.ln_gamma = at<const float>(14336);
+    k.ln_beta = at<const float>(16384);
+    k.ln_eps = 1e-6f;
+    k.flags = 0;
+    k.positions = at<const int64_t>(18432);
+    k.out_cache_loc = at<const int64_t>(20480);
+    k.num_tokens = T;
+    k.k_cache = at<uint8_t>(22528);
+    k.k_cache_row_stride = 128;
+    k.k_scale = at<float>(24576);
+    k.num_slots = 4096;
+    k.page_size = 0;
+    return k;
+}
+
+// Runs f (which must return DSAIDX_ERR_INVALID_ARGUMENT) and checks that it
+// enqueued nothing.
+template <typename F>
+void expect_rejected(F f, int line) {
+    const size_t before = g_launches.size();
+    const dsaidx_status st = f();
+    if (st != DSAIDX_ERR_INVALID_ARGUMENT || g_launches.size() != before) {
+        std::fprintf(stderr, "FAILED line %d: status %d, launches %zu -> %zu\n", line, (int)st, before,
+                     g_launches.size());
+        ++g_errors;
+    }
+}
+#define REJECT(expr) expect_rejected([&] { return (expr); }, __LINE__)
+
+void abi_and_status() {
+    CHECK(dsaidx_abi_version() == 3);
+    const dsaidx_status all[] = {DSAIDX_OK, DSAIDX_ERR_INVALID_ARGUMENT, DSAIDX_ERR_UNSUPPORTED,
+                                 DSAIDX_ERR_HIP};
+    for (dsaidx_status s : all) {
+        const char* t = dsaidx_status_string(s);
+        CHECK(t != nullptr && std::strlen(t) > 0);
+    }
+    CHECK(dsaidx_device_supported(0) == 0);
+    CHECK(dsaidx_device_supported(-1) == 0);
+}
+
+void launch_shapes() {
+    const dsaidx_rope rope = make_rope();
+    // fused, small batch: 4-head items, T * H = 320 query rows
+    {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(5, 64);
+        dsaidx_k_args k = make_k(5);
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1);
+        const Launch& l = g_launches[0];
+        CHECK(l.kind == 0 && l.block == 256 && l.style == DSAIDX_ROPE_NEOX);
+        CHECK(l.p.heads_per_item == 4 && l.p.head_blocks == 16 && l.p.q_items == 80);
+        CHECK(l.p.k_items == 2 && l.p.k_blocks == 1 && l.grid == 20 + 1);
+        CHECK(l.p.T == 5 && l.p.H == 64 && l.p.R == 64 && l.p.P == 4096 && l.p.rs == 32);
+        CHECK(l.p.page_size == 0 && l.p.S == 4096 && l.p.eps == 1e-6f && l.p.q_scale == nullptr);
+    }
+    // fused, large batch: 16-head items; key workgroups capped at 1/16 of the query ones
+    {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(300, 64);
+        dsaidx_k_args k = make_k(300);
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1);
+        const Launch& l = g_launches[0];
+        CHECK(l.p.heads_per_item == 16 && l.p.head_blocks == 4 && l.p.q_items == 1200);
+        CHECK(l.p.k_items == 75 && l.p.k_blocks == 19 && l.grid == 300 + 19);
+    }
+    // query side alone, interleaved rope, odd head count
+    {
+        g_launches.clear();
+        dsaidx_rope r2 = rope;
+        r2.style = DSAIDX_ROPE_INTERLEAVED;
+        dsaidx_q_args q = make_q(7, 5);
+        q.q_scale_out = at<float>(26624);
+        CHECK(dsaidx_q_rope_quant_fold(&q, &r2, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1);
+        const Launch& l = g_launches[0];
+        CHECK(l.style == DSAIDX_ROPE_INTERLEAVED && l.p.k_blocks == 0 && l.p.k_items == 0);
+        CHECK(l.p.head_blocks == 2 && l.p.q_items == 14 && l.grid == 4 && l.p.q_scale != nullptr);
+    }
+    // key side alone, and the k-only entry's one-wavefront workgroups
+    {
+        g_launches.clear();
+        dsaidx_k_args k = make_k(9);
+        CHECK(dsaidx_k_norm_rope_quant_store(&k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(dsaidx_k_only_prepare_store(&k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 2);
+        CHECK(g_launches[0].p.k_items == 3 && g_launches[0].grid == 1 && g_launches[0].block == 256);
+        CHECK(g_launches[0].p.q_items == 0 && g_launches[0].p.k_blocks == 1);
+        CHECK(g_launches[1].grid == 3 && g_launches[1].block == 64 && g_launches[1].p.k_blocks == 3);
+    }
+    // page-interleaved cache: no planar scale array needed
+    {
+        g_launches.clear();
+        dsaidx_k_args k = make_k(4);
+        k.flags = DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_INTERMEDIATE;
+        k.page_size = 64;
+        k.k_scale = nullptr;
+        k.k_cache_row_stride = 0;
+        CHECK(dsaidx_k_norm_rope_quant_store(&k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1 && g_launches[0].p.page_size == 64);
+        CHECK(g_launches[0].p.k_flags == (DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_INTERMEDIATE));
+    }
+    // no tokens: nothing enqueued, from any entry
+    {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(0, 64);
+        dsaidx_k_args k = make_k(0);
+        q.q = nullptr;  // not looked at when there is nothing to do
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(dsaidx_q_rope_quant_fold(&q, &rope, nullptr) == DSAIDX_OK);
+        CHECK(dsaidx_k_norm_rope_quant_store(&k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(dsaidx_k_only_prepare_store(&k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.empty());
+    }
+    // launch errors map to status codes
+    {
+        dsaidx_q_args q = make_q(3, 8);
+        g_fail = hipErrorNoBinaryForGpu;
+        CHECK(dsaidx_q_rope_quant_fold(&q, &rope, nullptr) == DSAIDX_ERR_UNSUPPORTED);
+        g_fail = hipErrorOutOfMemory;
+        CHECK(dsaidx_q_rope_quant_fold(&q, &rope, nullptr) == DSAIDX_ERR_HIP);
+        g_fail = hipSuccess;
+    }
+}
+
+void rejected_arguments() {
+    const dsaidx_rope rope = make_rope();
+    const dsaidx_q_args q0 = make_q(3, 8);
+    const dsaidx_k_args k0 = make_k(3);
+    g_launches.clear();
+    REJECT(dsaidx_q_rope_quant_fold(nullptr, &rope, nullptr));
+    REJECT(dsaidx_q_rope_quant_fold(&q0, nullptr, nullptr));
+    REJECT(dsaidx_qk_fused(&q0, nullptr, &rope, nullptr));
+    {
+        dsaidx_k_args k = k0;
+        k.num_tokens = 4;  // the two sides must agree
+        REJECT(dsaidx_qk_fused(&q0, &k, &rope, nullptr));
+    }
+    // rope table
+    auto bad_rope = [&](void (*edit)(dsaidx_rope&)) {
+        dsaidx_rope r = rope;
+        edit(r);
+        dsaidx_q_args q = q0;
+        dsaidx_k_args k = k0;
+        REJECT(dsaidx_q_rope_quant_fold(&q, &r, nullptr));
+        REJECT(dsaidx_k_norm_rope_quant_store(&k, &r, nullptr));
+        REJECT(dsaidx_qk_fused(&q, &k, &r, nullptr));
+    };
+    bad_rope([](dsaidx_rope& r) { r.cos = nullptr; });
+    bad_rope([](dsaidx_rope& r) { r.sin = at<const float>(1028); });      // not 16-byte aligned
+    bad_rope([](dsaidx_rope& r) { r.rope_dim = 0; });
+    bad_rope([](dsaidx_rope& r) { r.rope_dim = 24; });                    // not a multiple of 16
+    bad_rope([](dsaidx_rope& r) { r.rope_dim = 144; });
+    bad_rope([](dsaidx_rope& r) { r.style = 2; });
+    bad_rope([](dsaidx_rope& r) { r.row_stride = 16; });                  // < rope_dim / 2
+    bad_rope([](dsaidx_rope& r) { r.row_stride = 34; });                  // not a multiple of 4
+    bad_rope([](dsaidx_rope& r) { r.max_position = 0; });
+    // query side
+    auto bad_q = [&](void (*edit)(dsaidx_q_args&)) {
+        dsaidx_q_args q = q0;
+        edit(q);
+        dsaidx_k_args k = k0;
+        k.num_tokens = q.num_tokens;
+        REJECT(dsaidx_q_rope_quant_fold(&q, &rope, nullptr));
+        REJECT(dsaidx_qk_fused(&q, &k, &rope, nullptr));
+    };
+    bad_q([](dsaidx_q_args& q) { q.num_tokens = -1; });
+    bad_q([](dsaidx_q_args& q) { q.num_heads = 0; });
+    bad_q([](dsaidx_q_args& q) { q.num_heads = 4097; });
+    bad_q([](dsaidx_q_args& q) { q.weight_scale = INFINITY; });
+    bad_q([](dsaidx_q_args& q) { q.weight_scale = NAN; });
+    bad_q([](dsaidx_q_args& q) { q.q = nullptr; });
+    bad_q([](dsaidx_q_args& q) { q.weights = nullptr; });
+    bad_q([](dsaidx_q_args& q) { q.positions = nullptr; });
+    bad_q([](dsaidx_q_args& q) { q.q_fp8 = nullptr; });
+    bad_q([](dsaidx_q_args& q) { q.weights_out = nullptr; });
+    bad_q([](dsaidx_q_args& q) { q.q = at<const uint16_t>(2056); });      // 8-byte aligned only
+    bad_q([](dsaidx_q_args& q) { q.weights = at<const uint16_t>(4097); });
+    bad_q([](dsaidx_q_args& q) { q.positions = at<const int64_t>(6148); });
+    bad_q([](dsaidx_q_args& q) { q.q_fp8 = at<uint8_t>(8196); });
+    bad_q([](dsaidx_q_args& q) { q.weights_out = at<float>(10242); });
+    bad_q([](dsaidx_q_args& q) { q.q_scale_out = at<float>(26626); });
+    bad_q([](dsaidx_q_args& q) { q.q_stride_h = 120; });
+    bad_q([](dsaidx_q_args& q) { q.q_stride_h = 132; });                 // not a multiple of 8
+    bad_q([](dsaidx_q_args& q) { q.q_stride_t = 7 * 128 + 120; });      // rows would overlap
+    bad_q([](dsaidx_q_args& q) { q.q_stride_t = 8 * 128 + 4; });
+    bad_q([](dsaidx_q_args& q) { q.w_stride_t = 7; });
+    // key side
+    auto bad_k = [&](void (*edit)(dsaidx_k_args&)) {
+        dsaidx_k_args k = k0;
+        edit(k);
+        dsaidx_q_args q = q0;
+        q.num_tokens = k.num_tokens;
+        REJECT(dsaidx_k_norm_rope_quant_store(&k, &rope, nullptr));
+        REJECT(dsaidx_k_only_prepare_store(&k, &rope, nullptr));
+        REJECT(dsaidx_qk_fused(&q, &k, &rope, nullptr));
+    };
+    bad_k([](dsaidx_k_args& k) { k.num_tokens = -5; });
+    bad_k([](dsaidx_k_args& k) { k.k = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.ln_gamma = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.ln_beta = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.positions = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.out_cache_loc = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.k_cache = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.k_scale = nullptr; });
+    bad_k([](dsaidx_k_args& k) { k.k = at<const uint16_t>(12296); });
+    bad_k([](dsaidx_k_args& k) { k.ln_gamma = at<const float>(14340); });
+    bad_k([](dsaidx_k_args& k) { k.out_cache_loc = at<const int64_t>(20484); });
+    bad_k([](dsaidx_k_args& k) { k.k_scale = at<float>(24577); });
+    bad_k([](dsaidx_k_args& k) { k.k_stride_t = 64; });
+    bad_k([](dsaidx_k_args& k) { k.k_stride_t = 132; });
+    bad_k([](dsaidx_k_args& k) { k.ln_eps = 0.0f; });
+    bad_k([](dsaidx_k_args& k) { k.ln_eps = -1e-6f; });
+    bad_k([](dsaidx_k_args& k) { k.ln_eps = NAN; });
+    bad_k([](dsaidx_k_args& k) { k.ln_eps = INFINITY; });
+    bad_k([](dsaidx_k_args& k) { k.flags = 0x4; });
+    bad_k([](dsaidx_k_args& k) { k.num_slots = 0; });
+    bad_k([](dsaidx_k_args& k) { k.k_cache_row_stride = 120; });
+    bad_k([](dsaidx_k_args& k) { k.k_cache_row_stride = 132; });
+    bad_k([](dsaidx_k_args& k) {
+        k.flags = DSAIDX_K_PAGED_CACHE;
+        k.page_size = 96;  // does not divide num_slots = 4096
+    });
+    bad_k([](dsaidx_k_args& k) {
+        k.flags = DSAIDX_K_PAGED_CACHE;
+        k.page_size = 1;
+    });
+    bad_k([](dsaidx_k_args& k) {
+        k.flags = DSAIDX_K_PAGED_CACHE;
+        k.page_size = 3;
+        k.num_slots = 3 * 1024;
+    });
+    CHECK(g_launches.empty());
+}
+
+void topk_and_selftest() {
+    const float* lg = at<const float>(0);
+    int32_t* out = at<int32_t>(32768);
+    void* ws = at<void>(40960);
+    g_launches.clear();
+    CHECK(dsaidx_topk_per_row(lg, 1000, nullptr, 0, 1000, 10, out, nullptr, 0, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.empty());
+    CHECK(dsaidx_topk_workspace_bytes(3, 1000, 10) == 0);
+    CHECK(dsaidx_topk_workspace_bytes(3, 40000, 10) == 3 * (16416 + 8 * 4096));
+    CHECK(dsaidx_topk_workspace_bytes(3, 40000, 0) == -1);
+    CHECK(dsaidx_topk_workspace_bytes(-1, 40000, 10) == -1);
+    CHECK(dsaidx_topk_per_row(lg, 1000, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].kind == 1 && g_launches[0].rows == 3);
+    const int64_t need = 3 * (16416 + 8 * 4096);
+    CHECK(dsaidx_topk_per_row(lg, 40000, at<const int32_t>(1024), 3, 40000, 10, out, ws, need, nullptr) ==
+          DSAIDX_OK);
+    CHECK(g_launches.size() == 2 && g_launches[1].workspace == ws);
+    REJECT(dsaidx_topk_per_row(lg, 40000, nullptr, 3, 40000, 10, out, nullptr, need, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 40000, nullptr, 3, 40000, 10, out, at<void>(40968), need, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 40000, nullptr, 3, 40000, 10, out, ws, need - 1, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 1000, nullptr, 3, 1000, 0, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 1000, nullptr, 3, 1000, (1 << 20) + 1, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 1000, nullptr, -1, 1000, 10, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 996, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 1002, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(at<const float>(4), 1000, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 1000, at<const int32_t>(1026), 3, 1000, 10, out, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(lg, 1000, nullptr, 3, 1000, 10, nullptr, nullptr, 0, nullptr));
+    REJECT(dsaidx_topk_per_row(nullptr, 1000, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr));
+    g_launches.clear();
+    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 0, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.empty());
+    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 1000, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].kind == 2 && g_launches[0].grid == 1);
+    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), -1, nullptr));
+    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32772), 8, nullptr));
+    REJECT(dsaidx_fp8_encode_selftest(nullptr, at<uint8_t>(32768), 8, nullptr));
+}
+
+}  // namespace
+
+int main() {
+    abi_and_status();
+    launch_shapes();
+    rejected_arguments();
+    topk_and_selftest();
+    if (g_errors) {
+        std::fprintf(stderr, "%d check(s) failed\n", g_errors);
+        return 1;
+    }
+    std::printf("host layer: all checks passed\n");
+    return 0;
+}
