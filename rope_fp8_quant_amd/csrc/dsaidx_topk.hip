@@ -211,7 +211,7 @@ struct RowArgs {
     int64_t cols;
     int32_t k;
     int32_t* out;            // [rows, k]
-    int32_t solo;            // nonzero: wavefront 0 alone resolves a listed B1
+    int32_t many_rows;       // nonzero: several row workgroups per compute unit (see kManyRows)
 };
 
 constexpr int kCand = 1024;   // B1 logits kept in an LDS list (more: they stay in registers)
@@ -236,6 +236,20 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     const int wave = tid >> 6;
     const int32_t k = a.k;
     const int64_t r = blockIdx.x;
+    const float4* s4 = reinterpret_cast<const float4*>(a.logits + r * a.row_stride);
+    // Thread t's register group j holds logits 4 * (t + j * T) + 0..3.  In a
+    // call of few rows the groups are loaded before the row's length is
+    // known, up to the column count (one memory round trip less on the
+    // row's critical path); in a call of many rows only up to the length.
+    float4 f[V / 4];
+    if (!a.many_rows) {
+        const int32_t cols4 = (int32_t)((a.cols + 3) / 4);   // rows hold whole float4s
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) {
+            const int32_t c = tid + j * T;
+            f[j] = c < cols4 ? s4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
     int64_t len = a.cols;
     if (a.lengths) {
         const int64_t l = a.lengths[r];
@@ -246,7 +260,6 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         for (int64_t i = tid; i < k; i += T) dst[i] = i < len ? (int32_t)i : -1;
         return;
     }
-    const float* src = a.logits + r * a.row_stride;
     const int32_t n = (int32_t)len;          // <= T * V, checked on the host
 
     // Slot i of thread t holds logit pos(i); live(i) is false (for the whole
@@ -257,25 +270,28 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         if (slot < (uint32_t)k) dst[slot] = p;
     };
 
-    // ---- load, as order keys; key 0 marks a slot outside the row (no logit
-    // that is not NaN has key 0), so the count and write passes below need
-    // no bound checks.  Register group j (slots 4j..4j+3 of every thread) is
-    // full when all its slots lie inside the row, the same for the whole
-    // workgroup: only the group that straddles the row's end pays for
-    // per-slot checks.
+    // ---- order keys; key 0 marks a slot outside the row (no logit that is
+    // not NaN has key 0), so the count and write passes below need no bound
+    // checks.  Register group j is full when all its slots lie inside the
+    // row, the same for the whole workgroup: only the group that straddles
+    // the row's end pays for per-slot checks.
     auto full = [&](int j) -> bool { return (j + 1) * T * 4 <= n; };
     uint32_t key[V];
     {
-        const float4* s4 = reinterpret_cast<const float4*>(src);
+        if (a.many_rows) {
+#pragma unroll
+            for (int j = 0; j < V / 4; ++j) {
+                const int32_t c = tid + j * T;
+                f[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (full(j) || (live(4 * j) && 4 * c < n)) f[j] = s4[c];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < V / 4; ++j) {
-            const int32_t c = tid + j * T;
-            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (full(j) || (live(4 * j) && 4 * c < n)) f = s4[c];
-            key[4 * j + 0] = order_key(f.x);
-            key[4 * j + 1] = order_key(f.y);
-            key[4 * j + 2] = order_key(f.z);
-            key[4 * j + 3] = order_key(f.w);
+            key[4 * j + 0] = order_key(f[j].x);
+            key[4 * j + 1] = order_key(f[j].y);
+            key[4 * j + 2] = order_key(f[j].z);
+            key[4 * j + 3] = order_key(f[j].w);
         }
 #pragma unroll
         for (int j = 0; j < V / 4; ++j) {
@@ -399,7 +415,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     // share their top 11 bits; two radix passes on the 21 bits below (11,
     // then 10) give the rank-rem0 key.  Bin indices are masked so that they
     // stay inside the histograms whatever the list holds.
-    if (listed && a.solo) {
+    if (listed && a.many_rows) {
         if (wave != 0) return;
         const uint32_t base = b1 << 21;
         for (uint32_t c = lane; c < n1; c += 64)
@@ -839,19 +855,23 @@ struct TopkPlan {
 
 // Workgroup shapes (threads, logits per thread, waves per SIMD to leave room
 // for) of the row kernel for rows of up to 4096, 8192, 16384 and 32768 logits.
-// Capping the 512-thread shape at 64 VGPRs (8 waves per SIMD, a 12-byte spill)
-// measured 4 % faster on the causal prefill; the 1024-thread shapes spill more
-// under that cap and run slower.
-#define DSAIDX_TOPK_R4K 256, 16, 1
+// Capping the 512-thread shapes at 64 VGPRs (8 waves per SIMD) measured 4 %
+// faster on the causal prefill; the 1024-thread shapes spill under that cap
+// and run slower.  For rows of up to 4096 logits 512 x 8 beat 256 x 16 (which
+// LDS holds to six workgroups per compute unit): 18.9 against 23.5 us for
+// 4096 causal rows, equal on 64 rows.
+#define DSAIDX_TOPK_R4K 512, 8, 8
 #define DSAIDX_TOPK_R8K 512, 16, 8
 #define DSAIDX_TOPK_R16K 1024, 16, 1
 #define DSAIDX_TOPK_R32K 1024, 32, 1
 constexpr int64_t kRowMax = 32768;       // longest row of the row kernel
-// From this many rows (several row workgroups per compute unit) a long B1
-// list is resolved by one wavefront, which frees the compute unit for other
-// rows sooner; with fewer rows compute units idle, and every wavefront of the
-// row's workgroup shares that work to shorten the row's latency.
-constexpr int64_t kSoloRows = 1024;
+// From this many rows (several row workgroups per compute unit) the row
+// kernel works for throughput: a row's loads stop at its length, and a long
+// B1 list is resolved by one wavefront, which frees the compute unit for other
+// rows sooner.  With fewer rows compute units idle, and it works for latency:
+// the loads go out before the length is known, and every wavefront of the
+// row's workgroup shares the list work.
+constexpr int64_t kManyRows = 1024;
 
 static TopkPlan plan_topk(int64_t rows, int64_t cols, int32_t) {
     TopkPlan p{0, 0, 0, 0};
@@ -888,7 +908,7 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
                        hipStream_t stream) {
     const TopkPlan p = plan_topk(rows, cols, k);
     if (!p.split) {
-        RowArgs a{logits, row_stride, lengths, cols, k, out, rows >= kSoloRows ? 1 : 0};
+        RowArgs a{logits, row_stride, lengths, cols, k, out, rows >= kManyRows ? 1 : 0};
         switch (p.variant) {
             case 0: return launch_row<DSAIDX_TOPK_R4K>(a, rows, stream);
             case 1: return launch_row<DSAIDX_TOPK_R8K>(a, rows, stream);
