@@ -239,7 +239,7 @@ dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_r
  *   workspace_bytes  its size.
  * Logits must not be NaN.  One dispatch for rows of up to 32768 logits; four
  * for longer rows (the row spread over workgroups of 4096 logits, with the row's
- * histograms, counters and candidate list in the workspace); no allocation.
+ * histogram, counters and candidate list in the workspace); no allocation.
  * Calls that share a workspace must be ordered on one stream.  A workspace that
  * is required but NULL, misaligned or too small is DSAIDX_ERR_INVALID_ARGUMENT. */
 dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const int32_t* lengths,
@@ -248,10 +248,10 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
                                   dsaidx_stream_t stream);
 
 /* Bytes of workspace dsaidx_topk_per_row needs for this shape: 0 when
- * cols <= 32768, else rows * (16416 + 8 * L) with L = max(4096, cols / 16)
- * rounded up to a multiple of 4 (per row: two 2048-bin histograms and
- * counters, and a list of up to L candidate keys and indices; rows whose
- * threshold bin holds more are finished by re-reading the row); -1 for a
+ * cols <= 32768, else rows * (8224 + 8 * L) with L = max(4096, cols / 16)
+ * rounded up to a multiple of 4 (per row: a 2048-bin histogram and counters,
+ * and a list of up to L candidate keys and indices; rows whose threshold bin
+ * holds more are finished by re-reading the row); -1 for a
  * shape dsaidx_topk_per_row rejects
  * (including rows * ceil(cols / 4096) >= 2^31 when cols > 32768). */
 int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);

@@ -582,22 +582,24 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
 // Rows spread over one workgroup per chunk of 4096 logits, in four
 // dispatches over a caller workspace (the dispatch boundaries make each
 // step's global writes visible to the next; no fences or waits in kernels):
-//   zero:   the row's two 2048-bin histograms and counters;
+//   zero:   the row's 2048-bin histogram and counters;
 //   hist:   each chunk adds the histogram of its keys' top 11 bits (digit 1);
 //   select: each chunk finds the bin B1 of the k-th largest from the row's
 //           histogram, writes its logits above B1 at slots taken with one
-//           global atomic per workgroup, appends its B1 logits (key and index)
-//           to the row's list and adds their next 11 bits (digit 2) to the
-//           second histogram;
-//   finish: one workgroup per row finds digit 2 from the second histogram and
-//           the last 10 bits from an LDS histogram over the list, and writes
-//           the list's selected entries.  When B1 overflowed the list (its
+//           global atomic per workgroup and appends its B1 logits (key and
+//           index) to the row's list;
+//   finish: one workgroup per row finds the next 11 bits (digit 2) and then
+//           the last 10 from LDS histograms over the list, and writes the
+//           list's selected entries.  When B1 overflowed the list (its
 //           capacity is max(4096, cols / 16)), the finish streams the row
-//           instead: the digit-2 histogram counts every B1 logit either way.
+//           instead.
+// The select step adds nothing to a global digit-2 histogram: those device
+// atomics, contended by the row's chunks, cost it 2.1 of 15.1 us, more than
+// the finish's extra pass over the list.
 constexpr int kSplitT = 256;
 constexpr int kSplitV = 16;
 constexpr int kSplitChunk = kSplitT * kSplitV;
-constexpr int kStateWords = 2 * kBins + 8;    // two histograms, counters: placed, listed
+constexpr int kStateWords = kBins + 8;        // digit-1 histogram, counters: placed, listed
 
 struct SplitArgs {
     const float* logits;
@@ -675,10 +677,11 @@ __global__ __launch_bounds__(kSplitT) void topk_split_hist_kernel(SplitArgs a) {
     }
 }
 
-__global__ __launch_bounds__(kSplitT) void topk_split_select_kernel(SplitArgs a) {
+// Eight waves per SIMD: all chunk workgroups of 64 rows of 131072 are
+// resident at once (the register budget otherwise leaves seven).
+__global__ __launch_bounds__(kSplitT, 8) void topk_split_select_kernel(SplitArgs a) {
     constexpr int T = kSplitT;
     constexpr int W = T / 64;
-    __shared__ uint32_t hist[kBins];
     __shared__ uint32_t part[W];
     __shared__ uint32_t sel[2];
     __shared__ uint32_t shared_base[2];
@@ -698,12 +701,10 @@ __global__ __launch_bounds__(kSplitT) void topk_split_select_kernel(SplitArgs a)
     if (base >= lr) return;
     const int32_t n = (int32_t)(lr - base < kSplitChunk ? lr - base : kSplitChunk);
     uint32_t* g1 = a.state + r * kStateWords;
-    uint32_t* g2 = g1 + kBins;
-    uint32_t* ctrl = g2 + kBins;
+    uint32_t* ctrl = g1 + kBins;
     uint32_t* lk = a.list_key + r * a.list_stride;
     int32_t* lp = a.list_pos + r * a.list_stride;
 
-    for (int b = tid; b < kBins; b += T) hist[b] = 0;
     if (tid == 0) {
         sel[0] = 0;
         sel[1] = 1;
@@ -724,10 +725,7 @@ __global__ __launch_bounds__(kSplitT) void topk_split_select_kernel(SplitArgs a)
         if (key[i]) {
             const uint32_t d1 = key[i] >> 21;
             n_gt += d1 > b1 ? 1u : 0u;
-            if (d1 == b1) {
-                ++n_eq;
-                atomicAdd(&hist[(key[i] >> 10) & (kBins - 1)], 1u);
-            }
+            n_eq += d1 == b1 ? 1u : 0u;
         }
     }
     const uint32_t packed = n_gt | (n_eq << 16);             // chunk totals < 2^13
@@ -762,10 +760,6 @@ __global__ __launch_bounds__(kSplitT) void topk_split_select_kernel(SplitArgs a)
             }
         }
     }
-    for (int b = tid; b < kBins; b += T) {
-        const uint32_t c = hist[b];
-        if (c) atomicAdd(&g2[b], c);
-    }
 }
 
 // One workgroup per row: rank `rem` among the n1 listed B1 logits, from the
@@ -775,38 +769,41 @@ constexpr int kFinishT = 1024;
 __global__ __launch_bounds__(kFinishT) void topk_split_finish_kernel(SplitArgs a) {
     constexpr int T = kFinishT;
     constexpr int W = T / 64;
-    __shared__ uint32_t hist[kBins];
+    __shared__ __align__(16) uint32_t hist2[kBins];
+    __shared__ __align__(16) uint32_t hist3[1024];
     __shared__ uint32_t part[W];
     __shared__ uint32_t sel[2];
     __shared__ uint32_t cnt[2];
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int32_t k = a.k;
     const int64_t r = blockIdx.x;
     if (split_row_length(a, r) <= k) return;
     int32_t* dst = a.out + r * (int64_t)k;
     const uint32_t* g1 = a.state + r * kStateWords;
-    const uint32_t* g2 = g1 + kBins;
     const uint32_t* lk = a.list_key + r * a.list_stride;
     const int32_t* lp = a.list_pos + r * a.list_stride;
 
-    for (int b = tid; b < kBins; b += T) hist[b] = 0;
+    {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        for (int b = 4 * tid; b < kBins; b += 4 * T) *reinterpret_cast<uint4*>(&hist2[b]) = z;
+        for (int b = 4 * tid; b < 1024; b += 4 * T) *reinterpret_cast<uint4*>(&hist3[b]) = z;
+    }
     if (tid < 2) cnt[tid] = 0;
     if (tid == 0) {
         sel[0] = 0;
         sel[1] = 1;
     }
-    uint32_t h1[kBins / T], h2[kBins / T];
+    uint32_t h1[kBins / T];
     load_bins<T>(g1, h1);
-    load_bins<T>(g2, h2);
-    uint32_t b1, rem, b2, rem2, b3, rem3;
+    uint32_t b1, rem;
     select_bin_regs<T>(h1, (uint32_t)k, part, sel, b1, rem);
     b1 = min(b1, (uint32_t)(kBins - 1));
     const uint32_t n1 = g1[b1];                              // every B1 logit of the row
     const bool listed = n1 <= (uint64_t)a.list_stride;
     const uint32_t above1 = (uint32_t)k - rem;
-    select_bin_regs<T>(h2, rem, part, sel, b2, rem2);
-    b2 = min(b2, (uint32_t)(kBins - 1));
     // The B1 logits: from the list, or, when it overflowed, by streaming the row.
     const int64_t lr = split_row_length(a, r);
     const float4* row4 = reinterpret_cast<const float4*>(a.logits + r * a.row_stride);
@@ -825,11 +822,35 @@ __global__ __launch_bounds__(kFinishT) void topk_split_finish_kernel(SplitArgs a
             }
         }
     };
-    for_b1([&](uint32_t kk, int32_t) {
-        if (((kk >> 10) & (kBins - 1)) == b2) atomicAdd(&hist[kk & 1023u], 1u);
-    });
+    // digit 2 (bits 20..10) and digit 3 (bits 9..0) of the rank-rem key; each
+    // digit is chosen by wavefront 0 and published behind one barrier (bin
+    // indices masked so that they stay inside the histograms)
+    for_b1([&](uint32_t kk, int32_t) { atomicAdd(&hist2[(kk >> 10) & (kBins - 1)], 1u); });
+    __syncthreads();                                         // also: every thread has read sel
+    if (wave == 0) {
+        uint32_t d, q;
+        wave_select<kBins>(hist2, rem, d, q);
+        if (lane == 0) {
+            sel[0] = d;
+            sel[1] = q;
+        }
+    }
     __syncthreads();
-    select_bin<T>(hist, rem2, part, sel, b3, rem3);
+    const uint32_t b2 = sel[0], rem2 = sel[1];
+    for_b1([&](uint32_t kk, int32_t) {
+        if (((kk >> 10) & (kBins - 1)) == b2) atomicAdd(&hist3[kk & 1023u], 1u);
+    });
+    __syncthreads();                                         // also: every thread has read sel
+    if (wave == 0) {
+        uint32_t d, q;
+        wave_select<1024>(hist3, rem2, d, q);
+        if (lane == 0) {
+            sel[0] = d;
+            sel[1] = q;
+        }
+    }
+    __syncthreads();
+    const uint32_t b3 = sel[0], rem3 = sel[1];
     const uint32_t kth = (b1 << 21) | (b2 << 10) | (b3 & 1023u);
     const uint32_t above = (uint32_t)k - rem3;
     for_b1([&](uint32_t kk, int32_t pos) {

@@ -87,7 +87,7 @@ int64_t topk_workspace_bytes(int64_t rows, int64_t cols, int32_t) {
     if (rows * ((cols + 4095) / 4096) >= (int64_t(1) << 31)) return -1;
     int64_t list = cols / 16 > 4096 ? cols / 16 : 4096;
     list = (list + 3) / 4 * 4;
-    return rows * (16416 + 8 * list);
+    return rows * (8224 + 8 * list);
 }
 
 }  // namespace dsaidx
@@ -382,12 +382,12 @@ void topk_and_selftest() {
     CHECK(dsaidx_topk_per_row(lg, 1000, nullptr, 0, 1000, 10, out, nullptr, 0, nullptr) == DSAIDX_OK);
     CHECK(g_launches.empty());
     CHECK(dsaidx_topk_workspace_bytes(3, 1000, 10) == 0);
-    CHECK(dsaidx_topk_workspace_bytes(3, 40000, 10) == 3 * (16416 + 8 * 4096));
+    CHECK(dsaidx_topk_workspace_bytes(3, 40000, 10) == 3 * (8224 + 8 * 4096));
     CHECK(dsaidx_topk_workspace_bytes(3, 40000, 0) == -1);
     CHECK(dsaidx_topk_workspace_bytes(-1, 40000, 10) == -1);
     CHECK(dsaidx_topk_per_row(lg, 1000, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr) == DSAIDX_OK);
     CHECK(g_launches.size() == 1 && g_launches[0].kind == 1 && g_launches[0].rows == 3);
-    const int64_t need = 3 * (16416 + 8 * 4096);
+    const int64_t need = 3 * (8224 + 8 * 4096);
     CHECK(dsaidx_topk_per_row(lg, 40000, at<const int32_t>(1024), 3, 40000, 10, out, ws, need, nullptr) ==
           DSAIDX_OK);
     CHECK(g_launches.size() == 2 && g_launches[1].workspace == ws);

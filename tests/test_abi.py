@@ -218,12 +218,12 @@ def test_topk_workspace_size_and_checks(L):
     ws = L.dsaidx_topk_workspace_bytes
     assert ws(64, 16384, 2048) == 0
     assert ws(64, 32768, 2048) == 0
-    # rows longer than 32768: per row two 2048-bin histograms and counters
-    # (16416 bytes) and a list of max(4096, cols / 16) (key, index) pairs
-    assert ws(64, 131072, 2048) == 64 * (16416 + 8 * 8192)
-    assert ws(3, 32769, 7) == 3 * (16416 + 8 * 4096)
-    assert ws(64, 50000, 40000) == 64 * (16416 + 8 * 4096)
-    assert ws(2, 1000003, 2048) == 2 * (16416 + 8 * 62500)
+    # rows longer than 32768: per row a 2048-bin histogram and counters
+    # (8224 bytes) and a list of max(4096, cols / 16) (key, index) pairs
+    assert ws(64, 131072, 2048) == 64 * (8224 + 8 * 8192)
+    assert ws(3, 32769, 7) == 3 * (8224 + 8 * 4096)
+    assert ws(64, 50000, 40000) == 64 * (8224 + 8 * 4096)
+    assert ws(2, 1000003, 2048) == 2 * (8224 + 8 * 62500)
     assert ws(0, 131072, 2048) == 0
     assert ws(-1, 10, 1) == -1 and ws(1, 10, 0) == -1 and ws(1, -1, 1) == -1
     assert ws(1 << 20, 1 << 30, 8) == -1      # grid of rows * ceil(cols / 4096) workgroups too large
