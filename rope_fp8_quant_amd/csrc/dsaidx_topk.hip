@@ -807,8 +807,26 @@ __global__ __launch_bounds__(kFinishT) void topk_split_finish_kernel(SplitArgs a
     // The B1 logits: from the list, or, when it overflowed, by streaming the row.
     const int64_t lr = split_row_length(a, r);
     const float4* row4 = reinterpret_cast<const float4*>(a.logits + r * a.row_stride);
+    // A list of up to kFinishRegs entries per thread is read into registers
+    // once (all its loads in flight together) for the three passes below.
+    constexpr int kFinishRegs = 8;
+    const bool in_regs = listed && n1 <= (uint32_t)(kFinishRegs * T);
+    uint32_t rk[kFinishRegs];
+    int32_t rp[kFinishRegs];
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kFinishRegs; ++i) {
+            const uint32_t c = tid + i * T;
+            rk[i] = c < n1 ? lk[c] : 0u;
+            rp[i] = c < n1 ? lp[c] : 0;
+        }
+    }
     auto for_b1 = [&](auto f) {
-        if (listed) {
+        if (in_regs) {
+#pragma unroll
+            for (int i = 0; i < kFinishRegs; ++i)
+                if ((uint32_t)(tid + i * T) < n1) f(rk[i], rp[i]);
+        } else if (listed) {
             for (uint32_t c = tid; c < n1; c += T) f(lk[c], lp[c]);
         } else {
             for (int64_t c = tid; 4 * c < lr; c += T) {
