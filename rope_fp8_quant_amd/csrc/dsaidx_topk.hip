@@ -12,27 +12,27 @@
 // Rows of up to 32768 logits (topk_row_kernel): one workgroup per row, each
 // thread holding V of the row's logits in registers for the whole selection,
 // so the row is read from HBM once and LDS holds only two 2048-bin histograms
-// and a short list.  The kernel is VALU-bound, so the per-logit work is kept
-// to integer compares on the keys:
+// and a short list.  The per-logit work is kept to integer compares on the
+// keys:
 //   1. a 2048-bin histogram of the keys' top 11 bits (sign, exponent, two
-//      mantissa bits); a scan from the top finds the bin B1 holding the k-th
-//      largest logit and its rank in B1;
+//      mantissa bits); wavefront 0 scans it from the top for the bin B1 that
+//      holds the k-th largest logit and its rank in B1;
 //   2. logits in bins above B1 are written, and B1's logits appended to an
 //      LDS list, at offsets from one workgroup prefix sum of both counts (no
 //      atomics);
 //   3. a list of at most 64 is ranked by one wavefront directly.  A longer
-//      one is radix-selected on 11-bit digits: in calls of many rows by one
-//      wavefront alone, on the 21 bits below B1's prefix (two passes, no
-//      workgroup barriers, the other wavefronts leave the compute unit to
-//      other rows); in smaller calls by the whole workgroup, on keys relative
-//      to the list's smallest key (most often one or two passes, none for a
-//      tie group).  When B1 overflows the list (a narrow value range), the
-//      workgroup selects over the registers.  The list's keys above the k-th
-//      and the needed keys equal to it fill the remaining slots.
+//      one is radix-selected on the 21 bits below B1's prefix, 11 then 10
+//      bits: in calls of many rows by wavefront 0 alone (no workgroup
+//      barriers; the other wavefronts leave the compute unit to other rows),
+//      in smaller calls by every wavefront adding to the digit histograms and
+//      wavefront 0 choosing each digit.  When B1 overflows the list (a narrow
+//      value range), the workgroup selects over the registers, on keys
+//      relative to B1's smallest key.  The list's keys above the k-th and the
+//      needed keys equal to it fill the remaining slots.
 // Linear bins between the row's min and max adapt better to a narrow value
 // range, but cost a min/max pass and about eight more instructions per logit:
 // 14.5 against 12.5 us for 64 rows of 16384, 75 against 72 us for the causal
-// 8192-row prefill.
+// 8192-row prefill (measured when adopted).
 // Longer rows take the split-row path below (four dispatches over a caller
 // workspace), which spreads one row over many workgroups.
 #include "dsaidx_internal.h"
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     __shared__ uint32_t part[W];
     __shared__ uint32_t red[2][W];
     __shared__ uint32_t sel[2];
-    __shared__ uint32_t cnt[3];              // list length, B1 outputs above / equal to the k-th
+    __shared__ uint32_t cnt[2];              // B1 outputs above / equal to the k-th
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         }
         if (tid < 16) *reinterpret_cast<uint4*>(&hist0[kBins + 4 * tid]) = z;
     }
-    if (tid < 3) cnt[tid] = 0;
+    if (tid < 2) cnt[tid] = 0;
     if (tid == 0) {
         sel[0] = 0;
         sel[1] = 1;
@@ -500,9 +500,9 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
         for (uint32_t c = tid; c < n1; c += T) {
             const uint32_t key = cand_key[c];
             if (key > kth) {
-                write(above0 + atomicAdd(&cnt[1], 1u), cand_pos[c]);
+                write(above0 + atomicAdd(&cnt[0], 1u), cand_pos[c]);
             } else if (key == kth) {
-                const uint32_t q = atomicAdd(&cnt[2], 1u);
+                const uint32_t q = atomicAdd(&cnt[1], 1u);
                 if (q < r2) write((uint32_t)k - r2 + q, cand_pos[c]);
             }
         }
@@ -569,9 +569,9 @@ __global__ __launch_bounds__(T, MINW) void topk_row_kernel(RowArgs a) {
     const uint32_t above = (uint32_t)k - rem;
     for_b1([&](uint32_t key, int32_t p) {
         if (key > kth) {
-            write(above0 + atomicAdd(&cnt[1], 1u), p);
+            write(above0 + atomicAdd(&cnt[0], 1u), p);
         } else if (key == kth) {
-            const uint32_t q = atomicAdd(&cnt[2], 1u);
+            const uint32_t q = atomicAdd(&cnt[1], 1u);
             if (q < rem) write(above + q, p);
         }
     });
