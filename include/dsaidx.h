@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DSAIDX_ABI_VERSION 3
+#define DSAIDX_ABI_VERSION 4
 #define DSAIDX_HEAD_DIM 128 /* width of every head vector and K row */
 
 typedef struct ihipStream_t* dsaidx_stream_t; /* the same type as hipStream_t */
@@ -256,6 +256,57 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
  * (including rows * ceil(cols / 4096) >= 2^31 when cols > 32768). */
 int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
 
+/* Index logits: the step that consumes the prepared query and the index-K
+ * cache, between the indexer prep and the top-k (the fp8 paged MQA-logits
+ * launch of [vllm-47335] Kernel-level evidence).  The pages name the step but
+ * do not write out its arithmetic; the reading taken is the one under which
+ * folding each head's query scale into its gate is exact -- a ReLU on each
+ * head's dot (it commutes with a positive factor), then a gate-weighted sum
+ * over the heads:
+ *   logits[t * logits_stride + s] =
+ *       kscale(slot) * sum_h weights[t * H + h] * max(0, sum_d q(t, h, d) * k(slot, d))
+ * with q(t, h, d) the E4M3FN value of q_fp8[(t * H + h) * 128 + d], k(slot, d)
+ * the value of code d of the slot's cache row, kscale(slot) its scale, and
+ * slot = key_slots ? key_slots[s] : s.  Products are exact in fp32; the
+ * 128-term sums and the head sum are fp32, in an order the library chooses.
+ *   q_fp8          E4M3FN codes [T, H, 128], contiguous (the prep call's q_fp8), 16-byte aligned
+ *   weights        fp32 [T, H], contiguous (the prep call's weights_out), 4-byte aligned
+ *   num_tokens     T >= 0
+ *   num_heads      H in [1, 64]
+ *   flags          0, or DSAIDX_K_PAGED_CACHE for the page-interleaved layout
+ *   k_cache, k_cache_row_stride, k_scale, num_slots, page_size
+ *                  the index-K cache, read only, as in dsaidx_k_args
+ *   key_slots      int32 [num_keys]: the cache slot of each key (a page table's
+ *                  flattening), 4-byte aligned; NULL: key s is slot s, and then
+ *                  num_keys <= num_slots.  A slot outside [0, num_slots) reads
+ *                  no memory and its logit is 0
+ *   num_keys       N in [0, 2^31)
+ *   lengths        int32 [T], 4-byte aligned: query t scores keys
+ *                  [0, min(max(lengths[t], 0), N)); NULL: all N
+ *   logits         out fp32: row t at logits + t * logits_stride, 4-byte aligned;
+ *                  entries past a row's length are not written
+ *   logits_stride  floats, >= N
+ * T == 0 or N == 0 returns DSAIDX_OK with no launch.  One dispatch. */
+typedef struct dsaidx_logits_args {
+    const uint8_t* q_fp8;
+    const float* weights;
+    int64_t num_tokens;
+    int32_t num_heads;
+    int32_t flags;
+    const uint8_t* k_cache;
+    int64_t k_cache_row_stride;
+    const float* k_scale;
+    int64_t num_slots;
+    int64_t page_size;
+    const int32_t* key_slots;
+    int64_t num_keys;
+    const int32_t* lengths;
+    float* logits;
+    int64_t logits_stride;
+} dsaidx_logits_args;
+
+dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* args, dsaidx_stream_t stream);
+
 /* Encode n fp32 values to E4M3FN bytes with the device conversion every
  * kernel above uses (round to nearest even), so the conversion can be checked
  * on its own against the format definition.  in: device fp32 [n], 4-byte
@@ -276,7 +327,8 @@ const char* dsaidx_status_string(dsaidx_status status);
 int dsaidx_abi_version(void);
 
 /* sizeof the argument structs as built (0 = dsaidx_rope, 1 = dsaidx_q_args,
- * 2 = dsaidx_k_args; anything else returns 0), for binding checks. */
+ * 2 = dsaidx_k_args, 3 = dsaidx_logits_args; anything else returns 0), for
+ * binding checks. */
 size_t dsaidx_struct_size(int which);
 
 #ifdef __cplusplus

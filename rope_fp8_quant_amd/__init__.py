@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     DSAIDX_ROPE_NEOX,
     DsaidxError,
     DsaidxKArgs,
+    DsaidxLogitsArgs,
     DsaidxQArgs,
     DsaidxRope,
     dsaidx_abi_version,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     dsaidx_fp8_encode_selftest,
     dsaidx_k_norm_rope_quant_store,
     dsaidx_k_only_prepare_store,
+    dsaidx_mqa_logits,
     dsaidx_q_rope_quant_fold,
     dsaidx_qk_fused,
     dsaidx_status_string,
@@ -29,6 +31,7 @@ from .binding import (  # noqa: F401
     dsaidx_topk_workspace_bytes,
     k_args,
     lib,
+    logits_args,
     q_args,
     rope_args,
 )

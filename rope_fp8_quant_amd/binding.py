@@ -27,7 +27,7 @@ PAGED_SLOT_BYTES = ROW + 4   # one code row and one fp32 scale per slot
 EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaidx_qk_fused",
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
             "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest",
-            "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes")
+            "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes", "dsaidx_mqa_logits")
 
 
 class DsaidxError(RuntimeError):
@@ -61,6 +61,17 @@ class DsaidxKArgs(ctypes.Structure):
                 ("num_slots", ctypes.c_int64), ("page_size", ctypes.c_int64)]
 
 
+class DsaidxLogitsArgs(ctypes.Structure):
+    _fields_ = [("q_fp8", ctypes.c_void_p), ("weights", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("k_cache", ctypes.c_void_p),
+                ("k_cache_row_stride", ctypes.c_int64), ("k_scale", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int64), ("page_size", ctypes.c_int64),
+                ("key_slots", ctypes.c_void_p), ("num_keys", ctypes.c_int64),
+                ("lengths", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+                ("logits_stride", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -81,7 +92,8 @@ def lib() -> ctypes.CDLL:
                                                             ctypes.POINTER(DsaidxRope), P]),
                            ("dsaidx_qk_fused", [ctypes.POINTER(DsaidxQArgs),
                                                 ctypes.POINTER(DsaidxKArgs),
-                                                ctypes.POINTER(DsaidxRope), P])):
+                                                ctypes.POINTER(DsaidxRope), P]),
+                           ("dsaidx_mqa_logits", [ctypes.POINTER(DsaidxLogitsArgs), P])):
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -100,7 +112,7 @@ def lib() -> ctypes.CDLL:
         L.dsaidx_abi_version.restype = ctypes.c_int
         L.dsaidx_struct_size.argtypes = [ctypes.c_int]
         L.dsaidx_struct_size.restype = ctypes.c_size_t
-        for which, cls in enumerate((DsaidxRope, DsaidxQArgs, DsaidxKArgs)):
+        for which, cls in enumerate((DsaidxRope, DsaidxQArgs, DsaidxKArgs, DsaidxLogitsArgs)):
             if L.dsaidx_struct_size(which) != ctypes.sizeof(cls):
                 raise RuntimeError("libdsaidx ABI mismatch for %s" % cls.__name__)
         _lib = L
@@ -211,6 +223,10 @@ def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None, workspac
            "dsaidx_topk_per_row")
 
 
+def dsaidx_mqa_logits(args: DsaidxLogitsArgs, stream=None) -> None:
+    _check(lib().dsaidx_mqa_logits(ctypes.byref(args), _stream_handle(stream)), "dsaidx_mqa_logits")
+
+
 # ------------------------------------------- struct builders from tensors ----
 
 def _ptr(t) -> int:
@@ -295,3 +311,42 @@ def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cach
     return DsaidxKArgs(_ptr(k), k.stride(0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps),
                        int(flags), _ptr(positions), _ptr(out_cache_loc), T, _ptr(k_cache),
                        row_stride, scale_ptr, S, int(page_size))
+
+
+def logits_args(q_fp8, weights, k_cache, logits, k_scale=None, key_slots=None, lengths=None,
+                flags: int = 0, page_size: int = 0, num_slots=None) -> DsaidxLogitsArgs:
+    """q_fp8: 1-byte [T, H, 128] contiguous (16-byte aligned); weights: float32
+    [T, H] contiguous; logits: float32 [T, N] with unit column stride (N keys);
+    key_slots: int32 [N] or None (key s is slot s); lengths: int32 [T] or
+    None.  The cache arguments are those of k_args (read only)."""
+    import torch
+    _need(q_fp8.element_size() == 1 and q_fp8.dim() == 3 and q_fp8.shape[2] == ROW
+          and q_fp8.is_contiguous(), "q_fp8 must be a contiguous 1-byte [T, H, 128] tensor")
+    T, H = q_fp8.shape[0], q_fp8.shape[1]
+    _need(weights.dtype == torch.float32 and tuple(weights.shape) == (T, H) and weights.is_contiguous(),
+          "weights must be contiguous float32 [T, H]")
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.shape[0] == T
+          and logits.stride(1) == 1, "logits must be float32 [T, N] with unit column stride")
+    N = logits.shape[1]
+    if key_slots is not None:
+        _need(key_slots.dtype == torch.int32 and key_slots.numel() == N and key_slots.is_contiguous(),
+              "key_slots must be contiguous int32 [N]")
+    if lengths is not None:
+        _need(lengths.dtype == torch.int32 and lengths.numel() == T and lengths.is_contiguous(),
+              "lengths must be contiguous int32 [T]")
+    _need(k_cache.element_size() == 1, "k_cache must be a 1-byte tensor")
+    if flags & DSAIDX_K_PAGED_CACHE:
+        _need(k_cache.is_contiguous(), "a paged k_cache must be contiguous")
+        S = int(num_slots) if num_slots is not None else k_cache.numel() // PAGED_SLOT_BYTES
+        _need(k_cache.numel() >= S * PAGED_SLOT_BYTES, "paged k_cache smaller than num_slots * 132")
+        row_stride = 0
+    else:
+        _need(k_cache.dim() == 2 and k_cache.shape[1] >= ROW and k_cache.stride(1) == 1,
+              "k_cache must be a 1-byte [S, >=128] tensor")
+        S = k_cache.shape[0]
+        _need(k_scale is not None and k_scale.dtype == torch.float32 and k_scale.numel() == S
+              and k_scale.is_contiguous(), "k_scale must be contiguous float32 [S]")
+        row_stride = k_cache.stride(0)
+    return DsaidxLogitsArgs(_ptr(q_fp8), _ptr(weights), T, H, int(flags), _ptr(k_cache), row_stride,
+                            _ptr(k_scale), S, int(page_size), _ptr(key_slots), N, _ptr(lengths),
+                            _ptr(logits), logits.stride(0) if T else N)

@@ -146,6 +146,20 @@ dsaidx_status launch(const PrepParams& p, int style, int64_t grid, unsigned bloc
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Keys per logits workgroup for T queries over N keys: enough workgroups to
+// fill the GPU (about 2048; each reads its 8 tokens' queries once), but at
+// least 256 keys each, in whole LDS stages.  *chunks receives ceil(N / chunk).
+int64_t logits_key_chunk(int64_t T, int64_t N, int64_t* chunks) {
+    const int64_t blocks = ceil_div(T, dsaidx::kLogitsTokensPerBlock);
+    const int64_t most = ceil_div(N, 256);
+    int64_t want = ceil_div(2048, blocks);
+    if (want > most) want = most;
+    if (want < 1) want = 1;
+    const int64_t chunk = ceil_div(ceil_div(N, want), dsaidx::kLogitsStageKeys) * dsaidx::kLogitsStageKeys;
+    *chunks = ceil_div(N, chunk);
+    return chunk;
+}
+
 int64_t capped_grid(int64_t items, unsigned block) {
     const int64_t need = ceil_div(items, block / 64);
     return need < kMaxGrid ? need : kMaxGrid;
@@ -254,6 +268,52 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
                                          workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t stream) {
+    if (!a || !token_count_ok(a->num_tokens) || a->num_keys < 0 || a->num_keys >= (int64_t(1) << 31))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (a->num_tokens == 0 || a->num_keys == 0) return DSAIDX_OK;
+    if (a->num_heads < 1 || a->num_heads > dsaidx::kLogitsMaxHeads) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!a->q_fp8 || !a->weights || !a->k_cache || !a->logits) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!aligned(a->q_fp8, 16) || !aligned(a->weights, 4) || !aligned(a->k_cache, 8) ||
+        !aligned(a->logits, 4) || (a->key_slots && !aligned(a->key_slots, 4)) ||
+        (a->lengths && !aligned(a->lengths, 4)))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (a->flags & ~DSAIDX_K_PAGED_CACHE) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (a->num_slots < 1) return DSAIDX_ERR_INVALID_ARGUMENT;
+    const bool paged = (a->flags & DSAIDX_K_PAGED_CACHE) != 0;
+    if (paged) {
+        if (a->page_size < 2 || a->page_size > (1 << 20) || a->page_size % 2 != 0 ||
+            a->num_slots % a->page_size != 0)
+            return DSAIDX_ERR_INVALID_ARGUMENT;
+    } else {
+        if (!a->k_scale || !aligned(a->k_scale, 4)) return DSAIDX_ERR_INVALID_ARGUMENT;
+        if (a->k_cache_row_stride < dsaidx::kRow || a->k_cache_row_stride % 8 != 0)
+            return DSAIDX_ERR_INVALID_ARGUMENT;
+    }
+    if (!a->key_slots && a->num_keys > a->num_slots) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (a->logits_stride < a->num_keys) return DSAIDX_ERR_INVALID_ARGUMENT;
+    dsaidx::LogitsParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = a->q_fp8;
+    p.w = a->weights;
+    p.T = a->num_tokens;
+    p.H = a->num_heads;
+    p.k_cache = a->k_cache;
+    p.k_row_stride = paged ? 0 : a->k_cache_row_stride;
+    p.k_scale = paged ? nullptr : a->k_scale;
+    p.S = a->num_slots;
+    p.page_size = paged ? a->page_size : 0;
+    p.key_slots = a->key_slots;
+    p.N = a->num_keys;
+    p.lengths = a->lengths;
+    p.out = a->logits;
+    p.out_stride = a->logits_stride;
+    p.chunk = logits_key_chunk(p.T, p.N, &p.chunks);
+    if (ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) * p.chunks >= (int64_t(1) << 31))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    return to_status(dsaidx::launch_logits(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,
                                          dsaidx_stream_t stream) {
     if (n < 0 || !in || !out || !aligned(in, 4) || !aligned(out, 8))
@@ -290,6 +350,7 @@ size_t dsaidx_struct_size(int which) {
         case 0: return sizeof(dsaidx_rope);
         case 1: return sizeof(dsaidx_q_args);
         case 2: return sizeof(dsaidx_k_args);
+        case 3: return sizeof(dsaidx_logits_args);
     }
     return 0;
 }

@@ -82,4 +82,31 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
 hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigned grid,
                                hipStream_t stream);
 
+// Index logits (one dispatch): queries of at most kLogitsMaxHeads heads
+// against num_keys keys of the index-K cache.
+constexpr int kLogitsMaxHeads = 64;
+constexpr int kLogitsTokensPerBlock = 8;     // query tokens per workgroup
+constexpr int kLogitsStageKeys = 64;         // keys per LDS stage; chunks are multiples
+
+struct LogitsParams {
+    const uint8_t* q;          // [T, H, 128] E4M3 codes
+    const float* w;            // [T, H] folded gates
+    int64_t T;
+    int32_t H;
+    const uint8_t* k_cache;
+    int64_t k_row_stride;      // planar: bytes per slot row
+    const float* k_scale;      // planar
+    int64_t S;                 // slots
+    int64_t page_size;         // page-interleaved layout: slots per page (0 = planar)
+    const int32_t* key_slots;  // [N] or null (key s = slot s)
+    int64_t N;
+    const int32_t* lengths;    // [T] or null
+    float* out;
+    int64_t out_stride;
+    int64_t chunk;             // keys per workgroup
+    int64_t chunks;            // key chunks: the grid is ceil(T / 8) * chunks
+};
+
+hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);
+
 }  // namespace dsaidx

@@ -15,8 +15,9 @@
 namespace {
 
 struct Launch {
-    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test
+    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test, 3 logits
     dsaidx::PrepParams p;
+    dsaidx::LogitsParams lp;
     int style;
     unsigned grid, block;
     int64_t rows, cols, row_stride, n;
@@ -77,6 +78,15 @@ hipError_t launch_fp8_selftest(const float*, uint8_t*, int64_t n, unsigned grid,
     l.kind = 2;
     l.n = n;
     l.grid = grid;
+    g_launches.push_back(l);
+    return g_fail;
+}
+
+hipError_t launch_logits(const LogitsParams& p, hipStream_t) {
+    Launch l;
+    std::memset(&l, 0, sizeof l);
+    l.kind = 3;
+    l.lp = p;
     g_launches.push_back(l);
     return g_fail;
 }
@@ -167,7 +177,7 @@ void expect_rejected(F f, int line) {
 #define REJECT(expr) expect_rejected([&] { return (expr); }, __LINE__)
 
 void abi_and_status() {
-    CHECK(dsaidx_abi_version() == 3);
+    CHECK(dsaidx_abi_version() == 4);
     const dsaidx_status all[] = {DSAIDX_OK, DSAIDX_ERR_INVALID_ARGUMENT, DSAIDX_ERR_UNSUPPORTED,
                                  DSAIDX_ERR_HIP};
     for (dsaidx_status s : all) {
@@ -415,8 +425,101 @@ void topk_and_selftest() {
 
 }  // namespace
 
+void logits_calls() {
+    auto make = [](int64_t T, int32_t H, int64_t N) {
+        dsaidx_logits_args a;
+        std::memset(&a, 0, sizeof a);
+        a.q_fp8 = at<const uint8_t>(0);
+        a.weights = at<const float>(8192);
+        a.num_tokens = T;
+        a.num_heads = H;
+        a.k_cache = at<const uint8_t>(16384);
+        a.k_cache_row_stride = 128;
+        a.k_scale = at<const float>(32768);
+        a.num_slots = 1 << 20;
+        a.num_keys = N;
+        a.logits = at<float>(40960);
+        a.logits_stride = N;
+        return a;
+    };
+    g_launches.clear();
+    // key chunks: enough workgroups (about 2048 of 8 tokens each), at least 256 keys, whole stages
+    {
+        dsaidx_logits_args a = make(64, 64, 16384);
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        a = make(8192, 64, 8192);
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        a = make(5, 3, 100);
+        a.key_slots = at<const int32_t>(48000);
+        a.lengths = at<const int32_t>(49000);
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 3);
+        CHECK(g_launches[0].kind == 3 && g_launches[0].lp.chunk == 256 && g_launches[0].lp.chunks == 64);
+        CHECK(g_launches[1].lp.chunk == 4096 && g_launches[1].lp.chunks == 2);
+        CHECK(g_launches[2].lp.chunk == 128 && g_launches[2].lp.chunks == 1);
+        CHECK(g_launches[2].lp.H == 3 && g_launches[2].lp.N == 100 && g_launches[2].lp.page_size == 0);
+        CHECK(g_launches[2].lp.key_slots != nullptr && g_launches[2].lp.lengths != nullptr);
+    }
+    // page-interleaved cache; empty calls
+    {
+        g_launches.clear();
+        dsaidx_logits_args a = make(4, 64, 300);
+        a.flags = DSAIDX_K_PAGED_CACHE;
+        a.page_size = 64;
+        a.k_scale = nullptr;
+        a.k_cache_row_stride = 0;
+        a.num_slots = 4096;
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1 && g_launches[0].lp.page_size == 64 && g_launches[0].lp.k_scale == nullptr);
+        a = make(0, 64, 300);
+        a.q_fp8 = nullptr;
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        a = make(4, 64, 0);
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1);
+    }
+    auto bad = [&](void (*edit)(dsaidx_logits_args&)) {
+        dsaidx_logits_args a = make(16, 64, 1000);
+        edit(a);
+        REJECT(dsaidx_mqa_logits(&a, nullptr));
+    };
+    REJECT(dsaidx_mqa_logits(nullptr, nullptr));
+    bad([](dsaidx_logits_args& a) { a.num_tokens = -1; });
+    bad([](dsaidx_logits_args& a) { a.num_keys = -1; });
+    bad([](dsaidx_logits_args& a) { a.num_keys = int64_t(1) << 31; a.logits_stride = a.num_keys; });
+    bad([](dsaidx_logits_args& a) { a.num_heads = 0; });
+    bad([](dsaidx_logits_args& a) { a.num_heads = 65; });
+    bad([](dsaidx_logits_args& a) { a.q_fp8 = nullptr; });
+    bad([](dsaidx_logits_args& a) { a.weights = nullptr; });
+    bad([](dsaidx_logits_args& a) { a.k_cache = nullptr; });
+    bad([](dsaidx_logits_args& a) { a.logits = nullptr; });
+    bad([](dsaidx_logits_args& a) { a.q_fp8 = at<const uint8_t>(8); });          // 8-byte aligned only
+    bad([](dsaidx_logits_args& a) { a.weights = at<const float>(8194); });
+    bad([](dsaidx_logits_args& a) { a.k_cache = at<const uint8_t>(16388); });
+    bad([](dsaidx_logits_args& a) { a.logits = at<float>(40962); });
+    bad([](dsaidx_logits_args& a) { a.key_slots = at<const int32_t>(48002); });
+    bad([](dsaidx_logits_args& a) { a.lengths = at<const int32_t>(49001); });
+    bad([](dsaidx_logits_args& a) { a.flags = DSAIDX_K_BF16_INTERMEDIATE; });
+    bad([](dsaidx_logits_args& a) { a.num_slots = 0; });
+    bad([](dsaidx_logits_args& a) { a.num_slots = 999; });                      // fewer slots than keys
+    bad([](dsaidx_logits_args& a) { a.logits_stride = 999; });
+    bad([](dsaidx_logits_args& a) { a.k_scale = nullptr; });
+    bad([](dsaidx_logits_args& a) { a.k_cache_row_stride = 120; });
+    bad([](dsaidx_logits_args& a) { a.k_cache_row_stride = 132; });
+    bad([](dsaidx_logits_args& a) {
+        a.flags = DSAIDX_K_PAGED_CACHE;
+        a.page_size = 96;                                                         // does not divide 2^20
+    });
+    bad([](dsaidx_logits_args& a) {
+        a.flags = DSAIDX_K_PAGED_CACHE;
+        a.page_size = 3;
+        a.num_slots = 3 << 10;
+    });
+}
+
 int main() {
     abi_and_status();
+    logits_calls();
     launch_shapes();
     rejected_arguments();
     topk_and_selftest();

@@ -46,10 +46,11 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_struct_sizes(L):
-    assert B.dsaidx_abi_version() == 3
+    assert B.dsaidx_abi_version() == 4
     assert L.dsaidx_struct_size(0) == ctypes.sizeof(B.DsaidxRope) == 40
     assert L.dsaidx_struct_size(1) == ctypes.sizeof(B.DsaidxQArgs) == 88
     assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 104
+    assert L.dsaidx_struct_size(3) == ctypes.sizeof(B.DsaidxLogitsArgs) == 112
     assert L.dsaidx_struct_size(7) == 0
 
 
@@ -256,6 +257,7 @@ int main(void) {
     if (dsaidx_struct_size(0) != sizeof(dsaidx_rope)) return 2;
     if (dsaidx_struct_size(1) != sizeof(dsaidx_q_args)) return 3;
     if (dsaidx_struct_size(2) != sizeof(dsaidx_k_args)) return 4;
+    if (dsaidx_struct_size(3) != sizeof(dsaidx_logits_args)) return 5;
     /* empty calls: OK without touching a device */
     if (dsaidx_qk_fused(&q, &k, &rope, NULL) != DSAIDX_OK) return 5;
     if (dsaidx_topk_per_row(NULL, 0, NULL, 0, 0, 1, NULL, NULL, 0, NULL) != DSAIDX_OK) return 6;
