@@ -40,6 +40,12 @@ def device_flags():
     return ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source device flags.  The logits kernel takes its MFMA results in
+# ordinary VGPRs (it reads every element back for the epilogue, so results in
+# AGPRs would cost a copy per element).
+SOURCE_FLAGS = {"dsaidx_logits.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False, extra_defines=(), out_path: str = LIB_PATH,
           build_dir: str = BUILD_DIR) -> str:
     """Compile every source and link libdsaidx.so; returns the library path.
@@ -52,7 +58,7 @@ def build(verbose: bool = False, extra_defines=(), out_path: str = LIB_PATH,
         obj = os.path.join(build_dir, src + ".o")
         cmd = [cc] + common_flags() + ["-D" + d for d in extra_defines]
         if src.endswith(".hip"):
-            cmd += device_flags() + ["-x", "hip"]
+            cmd += device_flags() + SOURCE_FLAGS.get(src, []) + ["-x", "hip"]
         cmd += ["-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -268,6 +268,21 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
                                          workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Division by the page size as a multiply and shift, exact for every
+// numerator below 2^31 (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994, with N = 31 bits): l = ceil(log2 d),
+// shift = 31 + l, magic = floor(2^shift / d) + 1.  Then magic * d - 2^shift
+// lies in (0, d] and d <= 2^l = 2^(shift - 31), which is the condition for
+// floor(n * magic / 2^shift) = floor(n / d); magic < 2^32 since d > 2^(l - 1).
+static void page_divisor(int64_t d, uint32_t* magic, int32_t* shift) {
+    int l = 0;
+    while ((int64_t(1) << l) < d) ++l;
+    const int s = 31 + l;
+    const unsigned __int128 m = ((unsigned __int128)1 << s) / (unsigned __int128)d + 1;
+    *magic = (uint32_t)m;
+    *shift = s;
+}
+
 dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t stream) {
     if (!a || !token_count_ok(a->num_tokens) || a->num_keys < 0 || a->num_keys >= (int64_t(1) << 31))
         return DSAIDX_ERR_INVALID_ARGUMENT;
@@ -303,6 +318,7 @@ dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t str
     p.k_scale = paged ? nullptr : a->k_scale;
     p.S = a->num_slots;
     p.page_size = paged ? a->page_size : 0;
+    if (paged) page_divisor(a->page_size, &p.page_magic, &p.page_shift);
     p.key_slots = a->key_slots;
     p.N = a->num_keys;
     p.lengths = a->lengths;

@@ -98,6 +98,8 @@ struct LogitsParams {
     const float* k_scale;      // planar
     int64_t S;                 // slots
     int64_t page_size;         // page-interleaved layout: slots per page (0 = planar)
+    uint32_t page_magic;       // slot / page_size = (slot * page_magic) >> page_shift
+    int32_t page_shift;        //   for every slot below 2^31
     const int32_t* key_slots;  // [N] or null (key s = slot s)
     int64_t N;
     const int32_t* lengths;    // [T] or null

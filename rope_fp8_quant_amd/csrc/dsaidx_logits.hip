@@ -19,9 +19,10 @@
 // their q rows and gates held in registers for the whole call) and one chunk
 // of keys.  Keys are staged through LDS 64 at a time (double-buffered, one
 // barrier per stage), so each 16-key block read from L2 feeds 8 tokens x 4
-// head blocks of MFMAs.  Per block: ReLU and gate on the 4 results of each
-// lane, a sum over the lane groups (two cross-lane exchanges), the key scale
-// and a store by 16 lanes.
+// head blocks of MFMAs.  Per block: the 8 MFMAs of a wavefront back to back,
+// then ReLU and gate on the 4 results of each lane, a sum over the lane groups
+// for both tokens together (two lane-swap instructions), the key scale and
+// one store of 16 keys per token.
 #include "dsaidx_internal.h"
 
 namespace dsaidx {
@@ -35,6 +36,7 @@ constexpr int kLgTokensPerWave = kLogitsTokensPerBlock / 4;
 constexpr int kLgStage = kLogitsStageKeys;        // keys per LDS stage
 constexpr int kLgRowPitch = 144;                  // LDS bytes per staged key row (128 + 16: no bank conflicts)
 constexpr int kLgHeadBlocks = kLogitsMaxHeads / 16;
+static_assert(kLgTokensPerWave == 2, "the lane-group reduction pairs a wavefront's two tokens");
 
 // 16 x 16 x 128 block of dots over E4M3 codes (format 0 for both operands,
 // no block scales).  Lane l supplies row l % 16 of A and column l % 16 of B,
@@ -45,6 +47,9 @@ __device__ __forceinline__ v4f dots16(v8i a, v8i b) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
+
+// max(x, 0) in one instruction (v_med3_f32); the dots are finite.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.0e38f); }
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
     const uint4 a = *reinterpret_cast<const uint4*>(p);
@@ -70,8 +75,12 @@ __global__ __launch_bounds__(kLgThreads) void mqa_logits_kernel(LogitsParams p) 
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int g = lane >> 4;                      // lane group: bytes [32 g, 32 g + 32)
-    const int64_t tb = blockIdx.x / p.chunks;
-    const int64_t key0 = (blockIdx.x - tb * p.chunks) * p.chunk;
+    // token blocks from the last: under causal lengths the longest rows go
+    // first, so the short ones fill in behind them instead of trailing
+    const int64_t nb = (p.T + kLogitsTokensPerBlock - 1) / kLogitsTokensPerBlock;
+    const int64_t bi = blockIdx.x / p.chunks;
+    const int64_t tb = nb - 1 - bi;
+    const int64_t key0 = (blockIdx.x - bi * p.chunks) * p.chunk;
     const int64_t t_first = tb * kLogitsTokensPerBlock;
 
     // keys past every token's length are skipped (the same for the workgroup)
@@ -108,83 +117,95 @@ __global__ __launch_bounds__(kLgThreads) void mqa_logits_kernel(LogitsParams p) 
     }
 
     // stage loader: thread tid brings key tid / 4 of a stage, bytes
-    // [32 (tid % 4), +32) as four 8-byte loads, and lanes 0..63 the scales;
-    // a key past kend or with a slot outside the cache is all zeros
+    // [32 (tid % 4), +32) as four 8-byte loads, and the thread with tid % 4 = 0
+    // the key's scale; a key past kend or with a slot outside the cache is all
+    // zeros.  The slot index of a key is read one stage ahead of its row.
     const int sk = tid >> 2, sp = tid & 3;
+    auto slot_of = [&](int64_t s) -> int64_t {
+        if (s >= kend) return -1;
+        return p.key_slots ? (int64_t)p.key_slots[s] : s;
+    };
     uint2 sreg[4];
     float sscale = 0.f;
-    auto fetch = [&](int64_t s0) {
-        const int64_t s = s0 + sk;
-        int64_t slot = -1;
-        if (s < kend) slot = p.key_slots ? (int64_t)p.key_slots[s] : s;
+    auto fetch = [&](int64_t slot) {
         const bool ok = slot >= 0 && slot < p.S;
         const uint8_t* row = nullptr;
+        const float* scl = nullptr;
         if (ok) {
             if (p.page_size) {
-                const int64_t pg = slot / p.page_size, o = slot - pg * p.page_size;
-                row = p.k_cache + pg * p.page_size * 132 + o * 128;
+                const uint32_t pg = (uint32_t)(((uint64_t)slot * p.page_magic) >> p.page_shift);
+                const int64_t o = slot - (int64_t)pg * p.page_size;
+                const uint8_t* page = p.k_cache + (int64_t)pg * p.page_size * 132;
+                row = page + o * 128;
+                scl = reinterpret_cast<const float*>(page + p.page_size * 128) + o;
             } else {
                 row = p.k_cache + slot * p.k_row_stride;
+                scl = p.k_scale + slot;
             }
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             sreg[m] = ok ? *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * m) : make_uint2(0u, 0u);
-        if (tid < kLgStage) {
-            const int64_t s2 = s0 + tid;
-            int64_t slot2 = -1;
-            if (s2 < kend) slot2 = p.key_slots ? (int64_t)p.key_slots[s2] : s2;
-            sscale = 0.f;
-            if (slot2 >= 0 && slot2 < p.S) {
-                if (p.page_size) {
-                    const int64_t pg = slot2 / p.page_size, o = slot2 - pg * p.page_size;
-                    sscale = *reinterpret_cast<const float*>(p.k_cache + pg * p.page_size * 132 +
-                                                             p.page_size * 128 + o * 4);
-                } else {
-                    sscale = p.k_scale[slot2];
-                }
-            }
-        }
+        if (sp == 0) sscale = ok ? *scl : 0.f;
     };
     auto stash = [&](int buf) {
         uint8_t* d = &kbuf[buf][sk * kLgRowPitch + 32 * sp];
 #pragma unroll
         for (int m = 0; m < 4; ++m) *reinterpret_cast<uint2*>(d + 8 * m) = sreg[m];
-        if (tid < kLgStage) kscl[buf][tid] = sscale;
+        if (sp == 0) kscl[buf][sk] = sscale;
     };
 
-    fetch(key0);
+    // output: after the reduction lanes 0..15 hold token 0's sums and lanes
+    // 32..47 token 1's, for the 16 keys of a block (lane % 16)
+    const int oi = lane >> 5;
+    const bool writer = (lane & 16) == 0;
+    const int64_t otok = oi ? tok[1] : tok[0];
+    const int64_t olen = oi ? len[1] : len[0];
+    float* const orow = p.out + (otok < p.T ? otok : 0) * p.out_stride;
+
+    fetch(slot_of(key0 + sk));
+    int64_t slot_next = slot_of(key0 + kLgStage + sk);
     int buf = 0;
 #pragma unroll 1
     for (int64_t s0 = key0; s0 < kend; s0 += kLgStage, buf ^= 1) {
         stash(buf);
         __syncthreads();        // the stage is in LDS; every wavefront is done with the other buffer
-        if (s0 + kLgStage < kend) fetch(s0 + kLgStage);
+        if (s0 + kLgStage < kend) {
+            fetch(slot_next);
+            slot_next = slot_of(s0 + 2 * kLgStage + sk);
+        }
 #pragma unroll
         for (int kb = 0; kb < kLgStage / 16; ++kb) {
-            if (s0 + kb * 16 >= kend) break;
             const v8i B = load32(&kbuf[buf][(kb * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
+            // all dots of the block first (independent MFMAs in flight
+            // together), then the epilogue; heads past H have zero rows and
+            // gates and keys past kend zero rows, so they add nothing
+            v4f C[kLgTokensPerWave][kLgHeadBlocks];
+#pragma unroll
+            for (int i = 0; i < kLgTokensPerWave; ++i)
+#pragma unroll
+                for (int hb = 0; hb < kLgHeadBlocks; ++hb) C[i][hb] = dots16(A[i][hb], B);
             float acc[kLgTokensPerWave];
 #pragma unroll
             for (int i = 0; i < kLgTokensPerWave; ++i) {
                 acc[i] = 0.f;
 #pragma unroll
-                for (int hb = 0; hb < kLgHeadBlocks; ++hb) {
-                    if (hb * 16 >= p.H) break;
-                    const v4f c = dots16(A[i][hb], B);
-                    acc[i] += G[i][hb][0] * fmaxf(c[0], 0.f) + G[i][hb][1] * fmaxf(c[1], 0.f) +
-                              G[i][hb][2] * fmaxf(c[2], 0.f) + G[i][hb][3] * fmaxf(c[3], 0.f);
-                }
-            }
+                for (int hb = 0; hb < kLgHeadBlocks; ++hb)
 #pragma unroll
-            for (int i = 0; i < kLgTokensPerWave; ++i) {
-                float v = acc[i];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                const int64_t s = s0 + kb * 16 + (lane & 15);
-                if (lane < 16 && s < kend && s < len[i])
-                    p.out[tok[i] * p.out_stride + s] = v * kscl[buf][kb * 16 + lane];
+                    for (int e = 0; e < 4; ++e)
+                        acc[i] = __builtin_fmaf(G[i][hb][e], relu(C[i][hb][e]), acc[i]);
             }
+            // sum over the four lane groups for both tokens at once: the
+            // 32-lane swap pairs token 0's upper half with token 1's lower
+            // half, the 16-lane swap then folds the remaining pair of groups
+            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]),
+                                                            __float_as_uint(acc[1]), false, false);
+            const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+            const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2),
+                                                            false, false);
+            const float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+            const int64_t s = s0 + kb * 16 + (lane & 15);
+            if (writer && s < kend && s < olen) orow[s] = v * kscl[buf][kb * 16 + (lane & 15)];
         }
     }
 }
