@@ -13,7 +13,8 @@ Printed: one JSON line with tokens/s (value), ms per step, the HBM roofline
 of the kernel (algorithmic bytes / measured launch time against 8 TB/s), the
 oracle's CPU throughput on a bounded sample, and secondary measurements
 (decode-batch microseconds per call, the 8192-token prefill chunk with buffer
-rotation, the k-only decode path, a plain-copy bandwidth reference).
+rotation, the k-only decode path, the top-k per row and index-logits steps
+that follow, a plain-copy bandwidth reference).
 """
 from __future__ import annotations
 
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused indexer Q/K prep tokens/s and achieved HBM GB/s (% peak); \u00b5s/call"
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (no sparsity)
 WARM_MS = 100.0      # warm-up of the bandwidth-bound secondary measurements (GPU clock ramp)
 WARM_MS_LATENCY = 20.0   # the latency-bound decode ones (insensitive to it; keeps traces small)
 KERNEL_SOURCES = [os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", f)
@@ -212,6 +214,38 @@ def topk_measurements(torch, R, W, steps=50):
     return out
 
 
+def logits_measurements(torch, R, W, steps=20):
+    """Index logits (fp8 dots on the matrix cores, ReLU, gate-weighted head
+    sum, key scale) on the named synthetic workloads: microseconds per call and
+    achieved operations against the MI355X dense fp8 peak."""
+    out = {}
+    for li in range(len(W.LOGITS_NAMED)):
+        lw = W.logits_named(li)
+        T, H = lw.q_fp8.shape[:2]
+        N = len(lw.key_slots)
+        dq = torch.from_numpy(lw.q_fp8).cuda()
+        dw = torch.from_numpy(lw.weights).cuda()
+        dk = torch.from_numpy(lw.k_cache).cuda()
+        dks = torch.from_numpy(lw.k_scale).cuda()
+        dsl = torch.from_numpy(lw.key_slots).cuda()
+        dln = torch.from_numpy(lw.lengths).cuda()
+        lo = torch.empty((T, N), dtype=torch.float32, device="cuda")
+        args = R.logits_args(dq, dw, dk, lo, k_scale=dks, key_slots=dsl, lengths=dln)
+        call = lambda: R.dsaidx_mqa_logits(args)
+        mst = time_calls(torch, call, steps, 3, WARM_MS)
+        msg = time_graph(torch, call, 10, 5, WARM_MS)
+        fl = W.logits_flops_per_call(H, lw.lengths)
+        bt = W.logits_bytes_per_call(T, H, N, lw.lengths)
+        out[lw.name] = {"us_per_call": mst * 1e3, "us_per_call_graph": msg * 1e3,
+                        "T": T, "H": H, "keys": N,
+                        "algorithmic_ops": fl, "achieved_TOPs": fl / (mst * 1e-3) / 1e12,
+                        "frac_of_fp8_peak": fl / (mst * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                        "algorithmic_bytes": bt, "achieved_GBps": bt / (mst * 1e-3) / 1e9}
+        del dq, dw, dk, dks, dsl, dln, lo
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +256,8 @@ def main():
                     help="skip the decode, prefill-chunk and k-only measurements")
     ap.add_argument("--topk-only", action="store_true",
                     help="time only the top-k-per-row workloads (a JSON object of its own)")
+    ap.add_argument("--logits-only", action="store_true",
+                    help="time only the index-logits workloads (a JSON object of its own)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -240,6 +276,10 @@ def main():
         raise SystemExit("cuda:0 is not a gfx950 device")
     if args.topk_only:
         print(json.dumps({"topk_per_row": topk_measurements(torch, R, W, args.steps)}), flush=True)
+        return
+    if args.logits_only:
+        print(json.dumps({"mqa_logits": logits_measurements(torch, R, W, min(args.steps, 50))}),
+              flush=True)
         return
 
     log("generating long_prefill_T65536 inputs")
@@ -302,6 +342,11 @@ def main():
                                       "us_per_call_graph": ms_graph * 1e3,
                                       "bytes_per_call": W.bytes_per_call(64),
                                       "us_per_dispatch_floor_graph": ms_floor * 1e3}
+        # one token (the pages' single-request decode): graph replay
+        c1t = Case(W.named(1, T=1), torch, R)
+        ms_t1 = time_graph(torch, lambda: R.dsaidx_qk_fused(c1t.qa, c1t.ka, c1t.rope), 100, 20)
+        extras["decode_T1"] = {"us_per_call_graph": ms_t1 * 1e3, "bytes_per_call": W.bytes_per_call(1)}
+        del c1t
         # 512-token decode, interleaved RoPE: fused and k-only
         wl2 = W.named(2)
         c2 = Case(wl2, torch, R)
@@ -340,6 +385,7 @@ def main():
         del sets
         torch.cuda.empty_cache()
         extras.update(topk_measurements(torch, R, W))
+        extras.update(logits_measurements(torch, R, W))
         result["secondary"] = extras
 
     # plain device copy of the same byte count: the reference for achievable

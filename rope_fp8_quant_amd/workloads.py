@@ -272,3 +272,82 @@ def topk_bytes_per_call(rows: int, lengths, k: int = 2048) -> int:
     """Algorithmic bytes: every valid logit read once, the length of each row,
     and k indices written per row."""
     return int(np.sum(np.asarray(lengths, dtype=np.int64))) * 4 + rows * 4 + rows * k * 4
+
+
+# -------------------------------------------------- index-logits inputs ----
+
+@dataclass
+class LogitsWorkload:
+    name: str
+    q_fp8: np.ndarray       # uint8 E4M3FN codes [T, H, 128]
+    weights: np.ndarray     # float32 [T, H] (folded head gates)
+    k_cache: np.ndarray     # uint8 [S, 128] index-K cache codes
+    k_scale: np.ndarray     # float32 [S] (powers of two)
+    key_slots: np.ndarray   # int32 [N]: cache slot of key s
+    lengths: np.ndarray     # int32 [T]: keys valid for token t
+
+
+def _random_codes(rng, shape) -> np.ndarray:
+    """Uniform E4M3FN bytes with the two NaN codes replaced by zero."""
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0
+    return c
+
+
+def logits_make(T: int, N: int, H: int = 64, *, num_slots: int = 262144, lengths: str = "full",
+                slots: str = "contiguous", seed: int = 0, name: str = "custom") -> LogitsWorkload:
+    """Prepared queries and an index-K cache for the index logits.  Codes are
+    uniform over the non-NaN E4M3FN bytes (every binade), key scales 2^-12..2^-3,
+    gates N(0,1) * 2^-10..2^-5 (the range of folded ue8m0 gates).
+    slots: "contiguous" (N slots from a random offset) or "random" (N distinct
+    slots of the cache).  lengths: "full", "ragged" (uniform in [N/2, N]) or
+    "causal" (token t of the last T of an N-key context sees N - T + 1 + t keys)."""
+    kids = np.random.SeedSequence(seed).spawn(6)
+    rq, rw, rk, rs, rl, rp = (np.random.default_rng(s) for s in kids)
+    q8 = _random_codes(rq, (T, H, ROW))
+    w = (rw.standard_normal((T, H), dtype=np.float32)
+         * np.exp2(rw.integers(-10, -4, size=(T, H))).astype(np.float32))
+    kc = _random_codes(rk, (num_slots, ROW))
+    ks = np.exp2(rk.integers(-12, -2, size=num_slots)).astype(np.float32)
+    if slots == "contiguous":
+        off = int(rp.integers(0, num_slots - N + 1))
+        ksl = np.arange(off, off + N, dtype=np.int32)
+    elif slots == "random":
+        ksl = rp.permutation(num_slots)[:N].astype(np.int32)
+    else:
+        raise ValueError(slots)
+    if lengths == "full":
+        lens = np.full(T, N, np.int32)
+    elif lengths == "ragged":
+        lens = rl.integers(N // 2, N + 1, T).astype(np.int32)
+    elif lengths == "causal":
+        lens = (N - T + 1 + np.arange(T)).astype(np.int32)
+    else:
+        raise ValueError(lengths)
+    return LogitsWorkload(name=name, q_fp8=q8, weights=w, k_cache=kc, k_scale=ks, key_slots=ksl,
+                          lengths=lens)
+
+
+LOGITS_NAMED = [
+    ("logits_decode_batch64_ctx16384", dict(T=64, N=16384, lengths="ragged", slots="random")),
+    ("logits_prefill_causal_T8192", dict(T=8192, N=8192, lengths="causal")),
+    ("logits_prefill_full_T8192", dict(T=8192, N=8192, lengths="full")),
+]
+
+
+def logits_named(idx: int) -> LogitsWorkload:
+    name, kw = LOGITS_NAMED[idx]
+    return logits_make(seed=3000 + idx, name=name, **kw)
+
+
+def logits_flops_per_call(H: int, lengths) -> int:
+    """Algorithmic operations: one 128-term dot (2 * 128 ops) per head and
+    valid (token, key) pair; the gate and head sum are not counted."""
+    return 2 * ROW * H * int(np.sum(np.asarray(lengths, dtype=np.int64)))
+
+
+def logits_bytes_per_call(T: int, H: int, N: int, lengths) -> int:
+    """Algorithmic bytes: q codes and gates read once, each key's 128 codes,
+    scale and slot index read once, each valid logit written once."""
+    return T * H * (ROW + 4) + N * (ROW + 4 + 4) + T * 4 + \
+        int(np.sum(np.asarray(lengths, dtype=np.int64))) * 4

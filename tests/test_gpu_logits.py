@@ -261,3 +261,39 @@ def test_invalid_arguments():
     a.logits_stride = 65
     with pytest.raises(R.DsaidxError):
         R.dsaidx_mqa_logits(a)
+
+
+@pytest.mark.parametrize("idx", range(len(W.LOGITS_NAMED)))
+def test_named_workloads_sampled_rows(idx):
+    """The benchmark's workloads at full size, in the launch the benchmark
+    times: every row's untouched tail checked, and sampled rows (first, last
+    and random ones) against the oracle entry by entry within the bound."""
+    lw = W.logits_named(idx)
+    T, H = lw.q_fp8.shape[:2]
+    N = len(lw.key_slots)
+    print("\n[case] logits %s T=%d H=%d N=%d" % (lw.name, T, H, N), flush=True)
+    dq, dw = torch.from_numpy(lw.q_fp8).cuda(), torch.from_numpy(lw.weights).cuda()
+    dk, dks = torch.from_numpy(lw.k_cache).cuda(), torch.from_numpy(lw.k_scale).cuda()
+    out = torch.full((T, N), SENTINEL, dtype=torch.float32, device="cuda")
+    args = R.logits_args(dq, dw, dk, out, k_scale=dks,
+                         key_slots=torch.from_numpy(lw.key_slots).cuda(),
+                         lengths=torch.from_numpy(lw.lengths).cuda())
+    R.dsaidx_mqa_logits(args)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    past = np.arange(N)[None, :] >= lw.lengths[:, None]
+    assert np.all(got[past] == np.float32(SENTINEL)), "entries past a row's length were written"
+    assert not np.any(got[~past] == np.float32(SENTINEL))
+    rng = np.random.default_rng(idx)
+    rows = sorted(set([0, T - 1] + list(rng.integers(0, T, 6))))
+    slots = lw.key_slots.astype(np.int64)
+    worst = 0.0
+    for r in rows:
+        want = LG.mqa_logits(lw.q_fp8[r:r + 1], lw.weights[r:r + 1], lw.k_cache, lw.k_scale,
+                             key_slots=slots, lengths=lw.lengths[r:r + 1])[0]
+        tol = bound(lw.q_fp8[r:r + 1], lw.weights[r:r + 1], lw.k_cache, lw.k_scale, slots)[0]
+        n = int(lw.lengths[r])
+        err = np.abs(got[r, :n].astype(np.float64) - want[:n])
+        assert np.all(err <= tol[:n]), (r, float(np.max(err / tol[:n])))
+        worst = max(worst, float(np.max(err / tol[:n])) if n else 0.0)
+    print("[parity] %s rows %s: max err / bound %.3g" % (lw.name, rows, worst), flush=True)
