@@ -149,10 +149,16 @@ dsaidx_status launch(const PrepParams& p, int style, int64_t grid, unsigned bloc
 // Keys per logits workgroup for T queries over N keys: enough workgroups to
 // fill the GPU (about 2048; each reads its 8 tokens' queries once), but at
 // least 256 keys each, in whole LDS stages.  *chunks receives ceil(N / chunk).
+#ifndef DSAIDX_LG_TARGET_WGS
+#define DSAIDX_LG_TARGET_WGS 2048
+#endif
+#ifndef DSAIDX_LG_MIN_CHUNK
+#define DSAIDX_LG_MIN_CHUNK 256
+#endif
 int64_t logits_key_chunk(int64_t T, int64_t N, int64_t* chunks) {
     const int64_t blocks = ceil_div(T, dsaidx::kLogitsTokensPerBlock);
-    const int64_t most = ceil_div(N, 256);
-    int64_t want = ceil_div(2048, blocks);
+    const int64_t most = ceil_div(N, DSAIDX_LG_MIN_CHUNK);
+    int64_t want = ceil_div(DSAIDX_LG_TARGET_WGS, blocks);
     if (want > most) want = most;
     if (want < 1) want = 1;
     const int64_t chunk = ceil_div(ceil_div(N, want), dsaidx::kLogitsStageKeys) * dsaidx::kLogitsStageKeys;

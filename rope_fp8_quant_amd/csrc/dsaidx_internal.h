@@ -86,7 +86,11 @@ hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigne
 // against num_keys keys of the index-K cache.
 constexpr int kLogitsMaxHeads = 64;
 constexpr int kLogitsTokensPerBlock = 8;     // query tokens per workgroup
-constexpr int kLogitsStageKeys = 64;         // keys per LDS stage; chunks are multiples
+#ifndef DSAIDX_LG_KEYS_PER_THREAD
+#define DSAIDX_LG_KEYS_PER_THREAD 2
+#endif
+constexpr int kLogitsKeysPerThread = DSAIDX_LG_KEYS_PER_THREAD;   // key rows each thread stages
+constexpr int kLogitsStageKeys = 64 * kLogitsKeysPerThread;       // keys per LDS stage; chunks are multiples
 
 struct LogitsParams {
     const uint8_t* q;          // [T, H, 128] E4M3 codes

@@ -17,12 +17,18 @@
 //
 // Work: a workgroup of 4 wavefronts takes 8 query tokens (2 per wavefront,
 // their q rows and gates held in registers for the whole call) and one chunk
-// of keys.  Keys are staged through LDS 64 at a time (double-buffered, one
-// barrier per stage), so each 16-key block read from L2 feeds 8 tokens x 4
-// head blocks of MFMAs.  Per block: the 8 MFMAs of a wavefront back to back,
-// then ReLU and gate on the 4 results of each lane, a sum over the lane groups
-// for both tokens together (two lane-swap instructions), the key scale and
-// one store of 16 keys per token.
+// of keys.  Keys are staged through LDS 128 at a time (double-buffered, one
+// barrier per stage; each thread brings 32 bytes of two key rows), so each
+// 16-key block read from L2 feeds 8 tokens x 4 head blocks of MFMAs.  Per
+// block: the 8 MFMAs of a wavefront, the next block's key operand read from
+// LDS behind them, then ReLU and gate on the 4 results of each lane, a sum
+// over the lane groups for both tokens together (two lane-swap instructions),
+// the key scale and one store of 16 keys per token.
+//
+// Time on gfx950 goes to the matrix unit and the VALU in turn rather than
+// side by side, and the epilogue costs two VALU operations per dot (ReLU and
+// gate FMA): 64 per block and lane, as many cycles as the block's 8 MFMAs.
+// The register budget is held to three wavefronts per SIMD.
 #include "dsaidx_internal.h"
 
 namespace dsaidx {
@@ -67,7 +73,11 @@ __device__ __forceinline__ int64_t clamp_len(const LogitsParams& p, int64_t t) {
     return l < 0 ? 0 : (l < p.N ? l : p.N);
 }
 
-__global__ __launch_bounds__(kLgThreads) void mqa_logits_kernel(LogitsParams p) {
+#ifndef DSAIDX_LG_MIN_WAVES
+#define DSAIDX_LG_MIN_WAVES 3
+#endif
+__global__ __launch_bounds__(kLgThreads) __attribute__((amdgpu_waves_per_eu(DSAIDX_LG_MIN_WAVES)))
+void mqa_logits_kernel(LogitsParams p) {
     __shared__ __align__(16) uint8_t kbuf[2][kLgStage * kLgRowPitch];
     __shared__ float kscl[2][kLgStage];
 
@@ -121,91 +131,128 @@ __global__ __launch_bounds__(kLgThreads) void mqa_logits_kernel(LogitsParams p) 
     // the key's scale; a key past kend or with a slot outside the cache is all
     // zeros.  The slot index of a key is read one stage ahead of its row.
     const int sk = tid >> 2, sp = tid & 3;
-    auto slot_of = [&](int64_t s) -> int64_t {
+    constexpr int KPT = kLogitsKeysPerThread;
+    // the slot list is read one stage ahead into 32-bit registers and widened
+    // only when the row is fetched, so the wavefront never waits on it early
+    auto slot_of = [&](int64_t s, int32_t raw) -> int64_t {
         if (s >= kend) return -1;
-        return p.key_slots ? (int64_t)p.key_slots[s] : s;
+        return p.key_slots ? (int64_t)raw : s;
     };
-    uint2 sreg[4];
-    float sscale = 0.f;
-    auto fetch = [&](int64_t slot) {
-        const bool ok = slot >= 0 && slot < p.S;
-        const uint8_t* row = nullptr;
-        const float* scl = nullptr;
-        if (ok) {
-            if (p.page_size) {
-                const uint32_t pg = (uint32_t)(((uint64_t)slot * p.page_magic) >> p.page_shift);
-                const int64_t o = slot - (int64_t)pg * p.page_size;
-                const uint8_t* page = p.k_cache + (int64_t)pg * p.page_size * 132;
-                row = page + o * 128;
-                scl = reinterpret_cast<const float*>(page + p.page_size * 128) + o;
-            } else {
-                row = p.k_cache + slot * p.k_row_stride;
-                scl = p.k_scale + slot;
-            }
-        }
+    uint2 sreg[KPT][4];
+    float sscale[KPT];
+    auto fetch = [&](int64_t s0, const int32_t (&raw)[KPT]) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            sreg[m] = ok ? *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * m) : make_uint2(0u, 0u);
-        if (sp == 0) sscale = ok ? *scl : 0.f;
+        for (int j = 0; j < KPT; ++j) {
+            const int64_t slot = slot_of(s0 + 64 * j + sk, raw[j]);
+            const bool ok = slot >= 0 && slot < p.S;
+            const uint8_t* row = nullptr;
+            const float* scl = nullptr;
+            if (ok) {
+                if (p.page_size) {
+                    const uint32_t pg = (uint32_t)(((uint64_t)slot * p.page_magic) >> p.page_shift);
+                    const int64_t o = slot - (int64_t)pg * p.page_size;
+                    const uint8_t* page = p.k_cache + (int64_t)pg * p.page_size * 132;
+                    row = page + o * 128;
+                    scl = reinterpret_cast<const float*>(page + p.page_size * 128) + o;
+                } else {
+                    row = p.k_cache + slot * p.k_row_stride;
+                    scl = p.k_scale + slot;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                sreg[j][m] = ok ? *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * m) : make_uint2(0u, 0u);
+            sscale[j] = 0.f;
+            if (sp == 0) sscale[j] = ok ? *scl : 0.f;
+        }
     };
     auto stash = [&](int buf) {
-        uint8_t* d = &kbuf[buf][sk * kLgRowPitch + 32 * sp];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) *reinterpret_cast<uint2*>(d + 8 * m) = sreg[m];
-        if (sp == 0) kscl[buf][sk] = sscale;
+        for (int j = 0; j < KPT; ++j) {
+            uint8_t* d = &kbuf[buf][(sk + 64 * j) * kLgRowPitch + 32 * sp];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) *reinterpret_cast<uint2*>(d + 8 * m) = sreg[j][m];
+            if (sp == 0) kscl[buf][sk + 64 * j] = sscale[j];
+        }
+    };
+    auto slots_at = [&](int64_t s0, int32_t (&out)[KPT]) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int64_t s = s0 + 64 * j + sk;
+            out[j] = (p.key_slots && s < kend) ? p.key_slots[s] : -1;
+        }
     };
 
     // output: after the reduction lanes 0..15 hold token 0's sums and lanes
-    // 32..47 token 1's, for the 16 keys of a block (lane % 16)
+    // 32..47 token 1's, for the 16 keys of a block (lane % 16); key offsets
+    // from here on are relative to key0 (below the chunk size, 32-bit)
     const int oi = lane >> 5;
     const bool writer = (lane & 16) == 0;
     const int64_t otok = oi ? tok[1] : tok[0];
     const int64_t olen = oi ? len[1] : len[0];
-    float* const orow = p.out + (otok < p.T ? otok : 0) * p.out_stride;
+    const int64_t ostop = (olen < kend ? olen : kend) - key0;
+    const int lim = writer && ostop > 0 ? (int)ostop : 0;     // this lane stores keys rel < lim
+    float* const obase = p.out + (otok < p.T ? otok : 0) * p.out_stride + key0;
+    const int nkeys = (int)(kend - key0);
 
-    fetch(slot_of(key0 + sk));
-    int64_t slot_next = slot_of(key0 + kLgStage + sk);
+    // ReLU, gate and head sum of one block's dots, then the sum over the four
+    // lane groups for both tokens at once: the 32-lane swap pairs token 0's
+    // upper half with token 1's lower half, the 16-lane swap then folds the
+    // remaining pair of groups; key scale and store
+    auto epilogue = [&](const v4f (&C)[kLgTokensPerWave][kLgHeadBlocks], float ks, int rel) {
+        float acc[kLgTokensPerWave];
+#pragma unroll
+        for (int i = 0; i < kLgTokensPerWave; ++i) {
+            acc[i] = 0.f;
+#pragma unroll
+            for (int hb = 0; hb < kLgHeadBlocks; ++hb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[i] = __builtin_fmaf(G[i][hb][e], relu(C[i][hb][e]), acc[i]);
+        }
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]),
+                                                        __float_as_uint(acc[1]), false, false);
+        const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2),
+                                                        false, false);
+        const float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+        if (rel < lim) obase[rel] = v * ks;
+    };
+
+    int32_t slot_cur[KPT], slot_next[KPT];
+    slots_at(key0, slot_cur);
+    fetch(key0, slot_cur);
+    slots_at(key0 + kLgStage, slot_next);
     int buf = 0;
 #pragma unroll 1
-    for (int64_t s0 = key0; s0 < kend; s0 += kLgStage, buf ^= 1) {
+    for (int r0 = 0; r0 < nkeys; r0 += kLgStage, buf ^= 1) {
         stash(buf);
         __syncthreads();        // the stage is in LDS; every wavefront is done with the other buffer
-        if (s0 + kLgStage < kend) {
-            fetch(slot_next);
-            slot_next = slot_of(s0 + 2 * kLgStage + sk);
+        if (r0 + kLgStage < nkeys) {
+            fetch(key0 + r0 + kLgStage, slot_next);
+            slots_at(key0 + r0 + 2 * kLgStage, slot_next);
         }
+        // each block's key operand and scale are read from LDS one block ahead,
+        // so their latency hides behind the epilogue of the block before
+        v8i Bn = load32(&kbuf[buf][(lane & 15) * kLgRowPitch + 32 * g]);
+        float ksn = kscl[buf][lane & 15];
 #pragma unroll
         for (int kb = 0; kb < kLgStage / 16; ++kb) {
-            const v8i B = load32(&kbuf[buf][(kb * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
-            // all dots of the block first (independent MFMAs in flight
-            // together), then the epilogue; heads past H have zero rows and
-            // gates and keys past kend zero rows, so they add nothing
+            const v8i B = Bn;
+            const float ks = ksn;
+            const int rel = r0 + kb * 16 + (lane & 15);
+            // heads past H have zero rows and gates and keys past kend zero
+            // rows, so they add nothing
             v4f C[kLgTokensPerWave][kLgHeadBlocks];
 #pragma unroll
             for (int i = 0; i < kLgTokensPerWave; ++i)
 #pragma unroll
                 for (int hb = 0; hb < kLgHeadBlocks; ++hb) C[i][hb] = dots16(A[i][hb], B);
-            float acc[kLgTokensPerWave];
-#pragma unroll
-            for (int i = 0; i < kLgTokensPerWave; ++i) {
-                acc[i] = 0.f;
-#pragma unroll
-                for (int hb = 0; hb < kLgHeadBlocks; ++hb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[i] = __builtin_fmaf(G[i][hb][e], relu(C[i][hb][e]), acc[i]);
+            if (kb + 1 < kLgStage / 16) {
+                Bn = load32(&kbuf[buf][((kb + 1) * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
+                ksn = kscl[buf][(kb + 1) * 16 + (lane & 15)];
             }
-            // sum over the four lane groups for both tokens at once: the
-            // 32-lane swap pairs token 0's upper half with token 1's lower
-            // half, the 16-lane swap then folds the remaining pair of groups
-            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]),
-                                                            __float_as_uint(acc[1]), false, false);
-            const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-            const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2),
-                                                            false, false);
-            const float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
-            const int64_t s = s0 + kb * 16 + (lane & 15);
-            if (writer && s < kend && s < olen) orow[s] = v * kscl[buf][kb * 16 + (lane & 15)];
+            epilogue(C, ks, rel);
         }
     }
 }
