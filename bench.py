@@ -183,9 +183,19 @@ def cpu_baseline(wl, target_s=5.0, min_wall_s=1.2):
     while passes == 0 or total < min_wall_s:
         total += run(n)
         passes += 1
-    return dict(value=passes * n / total, unit="tokens/s", cores=cores, kind="oracle",
-                sample="first %d of %d tokens of %s (Q and K sides), %d pass(es), %.2f s wall on %d "
-                       "threads" % (n, wl.T, wl.name, passes, total, cores))
+    out = dict(value=passes * n / total, unit="tokens/s", cores=cores, kind="oracle",
+               sample="first %d of %d tokens of %s (Q and K sides), %d pass(es), %.2f s wall on %d "
+                      "threads" % (n, wl.T, wl.name, passes, total, cores))
+    # the same oracle on one thread, over a shorter leading slice
+    n1 = min(wl.T, 2048)
+    t0 = time.perf_counter()
+    oracle.q_side(wl.q[:n1], wl.weights[:n1], wl.positions[:n1], wl.cos, wl.sin, wl.rope_dim,
+                  wl.style, wl.weight_scale, nthreads=1)
+    oracle.k_side(wl.k[:n1], wl.gamma, wl.beta, wl.eps, wl.positions[:n1], wl.out_cache_loc[:n1],
+                  wl.cos, wl.sin, kc, ks, wl.rope_dim, wl.style, nthreads=1)
+    out["single_thread"] = {"value": n1 / (time.perf_counter() - t0), "unit": "tokens/s",
+                            "sample": "first %d tokens, 1 thread" % n1}
+    return out
 
 
 def topk_measurements(torch, R, W, steps=50):
