@@ -256,6 +256,37 @@ def logits_measurements(torch, R, W, steps=20):
     return out
 
 
+def decode_step_measurement(torch, R, W):
+    """One indexer decode step for a 64-request batch at a 16384-key context,
+    replayed from a HIP graph: the fused prep call (64 tokens into a
+    262144-slot index-K cache), the index logits over 16384 cache slots with
+    ragged lengths, and the top-k (k = 2048) per row."""
+    import numpy as np
+    lw = W.logits_named(0)
+    wl = W.make(64, 64, values="sparse_outliers", table_rows=8192, num_slots=lw.k_cache.shape[0],
+                slot_mode="random_distinct", seed=1001, name="decode_step_T64")
+    c = Case(wl, torch, R)
+    c.k_cache.copy_(torch.from_numpy(lw.k_cache))
+    c.k_scale.copy_(torch.from_numpy(lw.k_scale))
+    T, N, k = 64, len(lw.key_slots), 2048
+    dsl = torch.from_numpy(lw.key_slots).cuda()
+    dln = torch.from_numpy(lw.lengths).cuda()
+    lo = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    la = R.logits_args(c.q_fp8, c.w_out, c.k_cache, lo, k_scale=c.k_scale, key_slots=dsl, lengths=dln)
+    ws = torch.empty(max(R.dsaidx_topk_workspace_bytes(T, N, k), 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        R.dsaidx_qk_fused(c.qa, c.ka, c.rope)
+        R.dsaidx_mqa_logits(la)
+        R.dsaidx_topk_per_row(lo, k, idx, dln, workspace=ws)
+
+    ms = time_graph(torch, step, 20, 20)
+    del c, lo, idx, ws
+    torch.cuda.empty_cache()
+    return {"us_per_step_graph": ms * 1e3, "tokens": T, "keys": N, "k": k, "dispatches": 3}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +427,7 @@ def main():
         torch.cuda.empty_cache()
         extras.update(topk_measurements(torch, R, W))
         extras.update(logits_measurements(torch, R, W))
+        extras["decode_step_T64_ctx16384"] = decode_step_measurement(torch, R, W)
         result["secondary"] = extras
 
     # plain device copy of the same byte count: the reference for achievable

@@ -23,7 +23,7 @@ import torch
 
 import oracle
 import rope_fp8_quant_amd as R
-from gpu_util import DeviceCase
+from gpu_util import DeviceCase, logits_bound
 from oracle import logits as LG
 from rope_fp8_quant_amd import workloads as W
 
@@ -52,12 +52,7 @@ def random_query(T, H, rng):
 
 
 def bound(q8, w, codes, scale, slots):
-    dec = np.abs(LG.decode_table())
-    qa, ka = dec[q8], dec[codes[slots, :128]]
-    absdots = (qa.reshape(-1, 128) @ ka.T).reshape(q8.shape[0], q8.shape[1], -1)
-    per_dot = 2.0 ** -8 * qa.max(axis=2)[:, :, None] * ka.max(axis=1)[None, None, :] + 2.0 ** -16 * absdots
-    b = np.einsum("th,ths->ts", np.abs(w.astype(np.float64)), per_dot)
-    return b * scale.astype(np.float64)[slots][None, :] + 1e-30
+    return logits_bound(q8, w, codes, scale, slots)
 
 
 def run(q8, w, codes, scale, key_slots=None, lengths=None, N=None, paged_page=0, stride_pad=0):
@@ -285,7 +280,7 @@ def test_named_workloads_sampled_rows(idx):
     assert np.all(got[past] == np.float32(SENTINEL)), "entries past a row's length were written"
     assert not np.any(got[~past] == np.float32(SENTINEL))
     rng = np.random.default_rng(idx)
-    rows = sorted(set([0, T - 1] + list(rng.integers(0, T, 6))))
+    rows = sorted(set([0, T - 1] + [int(x) for x in rng.integers(0, T, 6)]))
     slots = lw.key_slots.astype(np.int64)
     worst = 0.0
     for r in rows:
