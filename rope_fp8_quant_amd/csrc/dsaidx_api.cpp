@@ -161,7 +161,8 @@ int64_t logits_key_chunk(int64_t T, int64_t N, int64_t* chunks) {
     int64_t want = ceil_div(DSAIDX_LG_TARGET_WGS, blocks);
     if (want > most) want = most;
     if (want < 1) want = 1;
-    const int64_t chunk = ceil_div(ceil_div(N, want), dsaidx::kLogitsStageKeys) * dsaidx::kLogitsStageKeys;
+    int64_t chunk = ceil_div(ceil_div(N, want), dsaidx::kLogitsStageKeys) * dsaidx::kLogitsStageKeys;
+    if (chunk > (int64_t(1) << 30)) chunk = int64_t(1) << 30;   // key offsets within a chunk are 32-bit
     *chunks = ceil_div(N, chunk);
     return chunk;
 }

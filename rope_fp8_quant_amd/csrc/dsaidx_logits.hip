@@ -126,14 +126,14 @@ void mqa_logits_kernel(LogitsParams p) {
         }
     }
 
-    // stage loader: thread tid brings key tid / 4 of a stage, bytes
-    // [32 (tid % 4), +32) as four 8-byte loads, and the thread with tid % 4 = 0
-    // the key's scale; a key past kend or with a slot outside the cache is all
-    // zeros.  The slot index of a key is read one stage ahead of its row.
+    // stage loader: thread tid brings keys tid / 4 + 64 j (j < KPT) of a
+    // stage, bytes [32 (tid % 4), +32) of each as four 8-byte loads, and the
+    // thread with tid % 4 = 0 their scales; a key past kend or with a slot
+    // outside the cache is all zeros.  The slot list is read one stage ahead
+    // into 32-bit registers and widened only when the rows are fetched, so
+    // the wavefront does not wait on it in the stage that loads it.
     const int sk = tid >> 2, sp = tid & 3;
     constexpr int KPT = kLogitsKeysPerThread;
-    // the slot list is read one stage ahead into 32-bit registers and widened
-    // only when the row is fetched, so the wavefront never waits on it early
     auto slot_of = [&](int64_t s, int32_t raw) -> int64_t {
         if (s >= kend) return -1;
         return p.key_slots ? (int64_t)raw : s;
