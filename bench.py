@@ -195,6 +195,21 @@ def cpu_baseline(wl, target_s=5.0, min_wall_s=1.2):
                   wl.cos, wl.sin, kc, ks, wl.rope_dim, wl.style, nthreads=1)
     out["single_thread"] = {"value": n1 / (time.perf_counter() - t0), "unit": "tokens/s",
                             "sample": "first %d tokens, 1 thread" % n1}
+    # the 64-token decode batch: median microseconds per call of 100
+    from rope_fp8_quant_amd import workloads as W
+    d = W.named(1)
+    dkc = np.zeros((d.num_slots, 128), np.uint8)
+    dks = np.zeros(d.num_slots, np.float32)
+    for label, nt in (("us_per_call_1_thread", 1), ("us_per_call_all_threads", cores)):
+        ts = []
+        for _ in range(100):
+            t0 = time.perf_counter()
+            oracle.q_side(d.q, d.weights, d.positions, d.cos, d.sin, d.rope_dim, d.style,
+                          d.weight_scale, nthreads=nt)
+            oracle.k_side(d.k, d.gamma, d.beta, d.eps, d.positions, d.out_cache_loc, d.cos, d.sin,
+                          dkc, dks, d.rope_dim, d.style, nthreads=nt)
+            ts.append(time.perf_counter() - t0)
+        out.setdefault("decode_batch_T64", {})[label] = sorted(ts)[50] * 1e6
     return out
 
 

@@ -200,8 +200,23 @@ def check_q(out: dict, wl: W.Workload, report: dict, tokens=None):
         compare_exact_f32(got_qs, qs, "q_scale")
 
 
+def k_rows_near_scale_boundary(wl: W.Workload, k_flags=0) -> int:
+    """Key rows whose amax (after LayerNorm and RoPE, in the oracle) lies within
+    4 fp32 ulps of a scale boundary 1.75 * 2^E, where a LayerNorm reduction
+    order different from the oracle's could move the ue8m0 exponent.  The
+    scales are still compared exactly; this count says how many rows that
+    exactness rests on the fp64 sums for."""
+    bf16_mode = 1 if k_flags & R.DSAIDX_K_BF16_INTERMEDIATE else 0
+    y, _ = oracle.k_values(wl.k, wl.gamma, wl.beta, wl.eps, wl.positions, wl.cos, wl.sin,
+                           wl.rope_dim, wl.style, bf16_mode)
+    ag = np.maximum(np.abs(y).max(axis=1), np.float32(1e-4)).astype(np.float32)
+    mant = (ag.view(np.uint32) & 0x7FFFFF).astype(np.int64)
+    return int(np.count_nonzero(np.abs(mant - 0x600000) <= 4))
+
+
 def check_k(out: dict, wl: W.Workload, report: dict, cache_row_pad=0, k_flags=0, page_size=0):
     kc, ks = oracle_k(wl, cache_row_pad, k_flags, page_size)
+    report["k_rows_near_scale_boundary"] = k_rows_near_scale_boundary(wl, k_flags)
     if k_flags & R.DSAIDX_K_PAGED_CACHE:
         got_kc, got_ks = split_paged(out["k_cache"], page_size, wl.num_slots)
     else:
