@@ -147,10 +147,11 @@ dsaidx_status launch(const PrepParams& p, int style, int64_t grid, unsigned bloc
 }
 
 // Keys per logits workgroup for T queries over N keys: enough workgroups to
-// fill the GPU (about 2048; each reads its 8 tokens' queries once), but at
-// least 256 keys each, in whole LDS stages.  *chunks receives ceil(N / chunk).
+// fill the GPU (about 3072, four rounds of the 768 that are resident at three
+// per CU; each reads its 8 tokens' queries once), but at least 256 keys each,
+// in whole LDS stages.  *chunks receives ceil(N / chunk).
 #ifndef DSAIDX_LG_TARGET_WGS
-#define DSAIDX_LG_TARGET_WGS 2048
+#define DSAIDX_LG_TARGET_WGS 3072
 #endif
 #ifndef DSAIDX_LG_MIN_CHUNK
 #define DSAIDX_LG_MIN_CHUNK 256
@@ -332,6 +333,7 @@ dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t str
     p.out = a->logits;
     p.out_stride = a->logits_stride;
     p.chunk = logits_key_chunk(p.T, p.N, &p.chunks);
+    p.chunk_major = ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) >= p.chunks ? 1 : 0;
     if (ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) * p.chunks >= (int64_t(1) << 31))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     return to_status(dsaidx::launch_logits(p, reinterpret_cast<hipStream_t>(stream)));

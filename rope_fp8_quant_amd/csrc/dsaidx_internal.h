@@ -111,6 +111,7 @@ struct LogitsParams {
     int64_t out_stride;
     int64_t chunk;             // keys per workgroup
     int64_t chunks;            // key chunks: the grid is ceil(T / 8) * chunks
+    int32_t chunk_major;       // workgroup order: chunk-major (1) or token-block-major (0)
 };
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);

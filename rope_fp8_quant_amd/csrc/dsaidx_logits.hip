@@ -88,9 +88,22 @@ void mqa_logits_kernel(LogitsParams p) {
     // token blocks from the last: under causal lengths the longest rows go
     // first, so the short ones fill in behind them instead of trailing
     const int64_t nb = (p.T + kLogitsTokensPerBlock - 1) / kLogitsTokensPerBlock;
-    const int64_t bi = blockIdx.x / p.chunks;
-    const int64_t tb = nb - 1 - bi;
-    const int64_t key0 = (blockIdx.x - bi * p.chunks) * p.chunk;
+    // The 8 XCDs take consecutive workgroups in turn.  Chunk-major order
+    // (consecutive workgroups: neighbouring token blocks of one chunk) gives
+    // every XCD its share of every chunk whatever the chunk count, which
+    // matters when chunks carry unequal work (causal lengths); token-major
+    // order (consecutive workgroups: the chunks of one token block) keeps each
+    // chunk's keys on one XCD when there are few token blocks and many chunks.
+    int64_t tb, key0;
+    if (p.chunk_major) {
+        const int64_t ci = blockIdx.x / nb;
+        tb = nb - 1 - (blockIdx.x - ci * nb);
+        key0 = ci * p.chunk;
+    } else {
+        const int64_t bi = blockIdx.x / p.chunks;
+        tb = nb - 1 - bi;
+        key0 = (blockIdx.x - bi * p.chunks) * p.chunk;
+    }
     const int64_t t_first = tb * kLogitsTokensPerBlock;
 
     // keys past every token's length are skipped (the same for the workgroup)

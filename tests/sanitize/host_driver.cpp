@@ -443,7 +443,8 @@ void logits_calls() {
         return a;
     };
     g_launches.clear();
-    // key chunks: enough workgroups (about 2048 of 8 tokens each), at least 256 keys, whole stages
+    // key chunks: enough workgroups (about 3072 of 8 tokens each), at least 256 keys, whole stages;
+    // chunk-major workgroup order when there are at least as many token blocks as chunks
     {
         dsaidx_logits_args a = make(64, 64, 16384);
         CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
@@ -455,7 +456,9 @@ void logits_calls() {
         CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
         CHECK(g_launches.size() == 3);
         CHECK(g_launches[0].kind == 3 && g_launches[0].lp.chunk == 256 && g_launches[0].lp.chunks == 64);
-        CHECK(g_launches[1].lp.chunk == 4096 && g_launches[1].lp.chunks == 2);
+        CHECK(g_launches[0].lp.chunk_major == 0);
+        CHECK(g_launches[1].lp.chunk == 2816 && g_launches[1].lp.chunks == 3);
+        CHECK(g_launches[1].lp.chunk_major == 1);
         CHECK(g_launches[2].lp.chunk == 128 && g_launches[2].lp.chunks == 1);
         CHECK(g_launches[2].lp.H == 3 && g_launches[2].lp.N == 100 && g_launches[2].lp.page_size == 0);
         CHECK(g_launches[2].lp.key_slots != nullptr && g_launches[2].lp.lengths != nullptr);
