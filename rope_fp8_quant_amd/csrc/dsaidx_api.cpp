@@ -334,6 +334,7 @@ dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t str
     p.out_stride = a->logits_stride;
     p.chunk = logits_key_chunk(p.T, p.N, &p.chunks);
     p.chunk_major = ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) >= p.chunks ? 1 : 0;
+    p.w_vec = (p.H % 4 == 0 && aligned(a->weights, 16)) ? 1 : 0;
     if (ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) * p.chunks >= (int64_t(1) << 31))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     return to_status(dsaidx::launch_logits(p, reinterpret_cast<hipStream_t>(stream)));

@@ -112,6 +112,7 @@ struct LogitsParams {
     int64_t chunk;             // keys per workgroup
     int64_t chunks;            // key chunks: the grid is ceil(T / 8) * chunks
     int32_t chunk_major;       // workgroup order: chunk-major (1) or token-block-major (0)
+    int32_t w_vec;             // H % 4 == 0 and weights 16-byte aligned: gates read 4 at a time
 };
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);

@@ -131,10 +131,18 @@ void mqa_logits_kernel(LogitsParams p) {
             const int h = hb * 16 + (lane & 15);
             A[i][hb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             if (t < p.T && h < p.H) A[i][hb] = load32(p.q + ((t * p.H + h) * 128 + 32 * g));
+            if (p.w_vec) {
+                // the lane's four gates are adjacent: one 16-byte load
+                float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (t < p.T && hb * 16 + 4 * g < p.H)
+                    gv = *reinterpret_cast<const float4*>(p.w + t * p.H + hb * 16 + 4 * g);
+                G[i][hb][0] = gv.x; G[i][hb][1] = gv.y; G[i][hb][2] = gv.z; G[i][hb][3] = gv.w;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int hh = hb * 16 + 4 * g + e;
-                G[i][hb][e] = (t < p.T && hh < p.H) ? p.w[t * p.H + hh] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int hh = hb * 16 + 4 * g + e;
+                    G[i][hb][e] = (t < p.T && hh < p.H) ? p.w[t * p.H + hh] : 0.f;
+                }
             }
         }
     }
