@@ -422,6 +422,19 @@ def main():
             "frac_of_peak": bytes_call / (msp * 1e-3) / 1e9 / PEAK_HBM_GBPS}
         del cp
         torch.cuda.empty_cache()
+        # a TP8 rank's share of the long prefill: 8 of the 64 heads (the key
+        # row has no head axis, so every rank prepares all of it)
+        wl8 = W.make(65536, 8, values="zero_rows", table_rows=262144, pos_mode="contiguous",
+                     pos_lo=196608, num_slots=262144, slot_mode="contiguous", seed=1004,
+                     name="long_prefill_T65536_H8")
+        c8 = Case(wl8, torch, R)
+        ms8 = time_calls(torch, lambda: R.dsaidx_qk_fused(c8.qa, c8.ka, c8.rope), 100, 10, WARM_MS)
+        b8 = W.bytes_per_call(wl8.T, 8)
+        extras["long_prefill_T65536_H8_tp8_share"] = {
+            "us_per_call": ms8 * 1e3, "bytes_per_call": b8, "achieved_GBps": b8 / (ms8 * 1e-3) / 1e9,
+            "frac_of_peak": b8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del c8, wl8
+        torch.cuda.empty_cache()
         # 8192-token prefill chunk: 4 rotating buffer sets (> 800 MB) so no
         # step finds its inputs in the last-level cache
         wl3 = W.named(3)

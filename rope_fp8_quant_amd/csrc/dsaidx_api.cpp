@@ -105,7 +105,8 @@ void fill_q(PrepParams& p, const dsaidx_q_args& q) {
     p.H = q.num_heads;
     p.heads_per_item = q.num_tokens * q.num_heads <= dsaidx::kSmallBatchHeadRows
                            ? dsaidx::kHeadsPerItemSmall
-                           : dsaidx::kHeadsPerItem;
+                           : (q.num_heads <= dsaidx::kHeadsPerItemMid ? dsaidx::kHeadsPerItemMid
+                                                                     : dsaidx::kHeadsPerItem);
     p.head_blocks = (q.num_heads + p.heads_per_item - 1) / p.heads_per_item;
     p.q_items = q.num_tokens * p.head_blocks;
     p.T = q.num_tokens;

@@ -26,7 +26,8 @@
 // query rows: a small batch cannot fill the GPU, and more, shorter items cut
 // its latency (64 tokens x 64 heads: 2.6 us against 3.0 us per call), while
 // for large batches 16-head items move fewer cos/sin rows and gates per byte
-// of q.  A key work item is 4 tokens.  Key and query work items share one
+// of q.  Large batches of at most 8 heads (a TP8 rank's share of 64) take
+// 8-head items, so that no row group of a wavefront idles.  A key work item is 4 tokens.  Key and query work items share one
 // dispatch: the last k_blocks workgroups take key items.
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
@@ -599,17 +600,25 @@ hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned b
                        hipStream_t stream) {
     PrepParams copy = p;
     void* args[] = {&copy};
-    const bool small = p.heads_per_item == kHeadsPerItemSmall;
+    const int hpi = p.heads_per_item;
+    auto pick = [hpi](auto k4, auto k8, auto k16) -> const void* {
+        return hpi == kHeadsPerItemSmall ? reinterpret_cast<const void*>(k4)
+               : hpi == kHeadsPerItemMid ? reinterpret_cast<const void*>(k8)
+                                         : reinterpret_cast<const void*>(k16);
+    };
     const void* fn;
     if (style == 1)
-        fn = small ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall>)
-                   : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem>);
+        fn = pick(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem>);
     else if (p.R <= 64)
-        fn = small ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall>)
-                   : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem>);
+        fn = pick(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemMid>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem>);
     else
-        fn = small ? reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall>)
-                   : reinterpret_cast<const void*>(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItem>);
+        fn = pick(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemMid>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItem>);
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream);
 }
 

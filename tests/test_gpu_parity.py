@@ -197,6 +197,26 @@ def test_head_counts(H):
     check_k(out, wl, rep)
 
 
+@pytest.mark.parametrize("H,style,rope_dim", [(8, W.NEOX, 64), (5, W.INTERLEAVED, 64), (1, W.NEOX, 128),
+                                               (3, W.NEOX, 96), (8, W.INTERLEAVED, 32), (12, W.NEOX, 64)])
+def test_head_counts_large_batches(H, style, rope_dim):
+    """More than 16384 query rows: 8-head items for at most 8 heads (a TP8
+    rank's share of 64), 16-head items above, with partly empty items."""
+    T = 16384 // H + 37
+    print("\n[case] large batch T=%d H=%d style=%d rope_dim=%d" % (T, H, style, rope_dim), flush=True)
+    wl = W.make(T, H, rope_dim=rope_dim, style=style, table_rows=4096, num_slots=T + 100,
+                slot_mode="perm_prefix", seed=300 + H + rope_dim)
+    c = DeviceCase(wl)
+    c.run("fused")
+    out = c.host()
+    rep = {}
+    check_q(out, wl, rep)
+    check_k(out, wl, rep)
+    c.run("q")
+    out2 = c.host()
+    assert np.array_equal(out2["q_fp8"], out["q_fp8"]) and np.array_equal(out2["w_out"], out["w_out"])
+
+
 @pytest.mark.parametrize("style", [W.NEOX, W.INTERLEAVED])
 @pytest.mark.parametrize("rope_dim", [16, 32, 48, 64, 80, 96, 112, 128])
 def test_rope_dims(rope_dim, style):
