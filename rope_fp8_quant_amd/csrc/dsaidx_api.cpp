@@ -105,10 +105,16 @@ void fill_q(PrepParams& p, const dsaidx_q_args& q) {
     p.H = q.num_heads;
     p.heads_per_item = q.num_tokens * q.num_heads <= dsaidx::kSmallBatchHeadRows
                            ? dsaidx::kHeadsPerItemSmall
-                           : (q.num_heads <= dsaidx::kHeadsPerItemMid ? dsaidx::kHeadsPerItemMid
+                           : (q.num_heads == dsaidx::kHeadsPerItemMid ? dsaidx::kHeadsPerItemMid
                                                                      : dsaidx::kHeadsPerItem);
-    p.head_blocks = (q.num_heads + p.heads_per_item - 1) / p.heads_per_item;
-    p.q_items = q.num_tokens * p.head_blocks;
+    if (p.heads_per_item == dsaidx::kHeadsPerItemMid) {
+        // items of two tokens x 8 heads
+        p.head_blocks = 1;
+        p.q_items = (q.num_tokens + 1) / 2;
+    } else {
+        p.head_blocks = (q.num_heads + p.heads_per_item - 1) / p.heads_per_item;
+        p.q_items = q.num_tokens * p.head_blocks;
+    }
     p.T = q.num_tokens;
 }
 
@@ -243,7 +249,10 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     fill_k(p, *k);
     const int64_t qb = capped_grid(p.q_items, kBlock);
     int64_t kb = ceil_div(p.k_items, kBlock / 64);
-    const int64_t kcap = ceil_div(qb, kKeyBlockDivisor);
+    // key rows are a small share of the bytes at 16 heads per item (a 16th of
+    // the query workgroups suffice); with 8 heads per token they are a sixth
+    const int64_t kcap = p.heads_per_item == dsaidx::kHeadsPerItemMid
+                             ? capped_grid(p.k_items, kBlock) : ceil_div(qb, kKeyBlockDivisor);
     if (kb > kcap) kb = kcap;
     p.k_blocks = (int32_t)kb;
     return launch(p, rope->style, qb + kb, kBlock, stream);

@@ -14,7 +14,7 @@ constexpr int kRowsPerWave = 4;     // 64 lanes / 16
 // cut the latency of a call that cannot fill the GPU.
 constexpr int kHeadsPerItem = 16;
 constexpr int kHeadsPerItemSmall = 4;
-constexpr int kHeadsPerItemMid = 8;   // large batches of at most 8 heads (a TP8 rank's share of 64)
+constexpr int kHeadsPerItemMid = 8;   // large batches of exactly 8 heads: items of 2 tokens x 8 heads
 constexpr int64_t kSmallBatchHeadRows = 16384;
 constexpr int kTokensPerKItem = 4;  // key rows per wavefront work item
 constexpr int32_t kKeyBf16Intermediate = 0x1;  // DSAIDX_K_BF16_INTERMEDIATE

@@ -26,8 +26,8 @@
 // query rows: a small batch cannot fill the GPU, and more, shorter items cut
 // its latency (64 tokens x 64 heads: 2.6 us against 3.0 us per call), while
 // for large batches 16-head items move fewer cos/sin rows and gates per byte
-// of q.  Large batches of at most 8 heads (a TP8 rank's share of 64) take
-// 8-head items, so that no row group of a wavefront idles.  A key work item is 4 tokens.  Key and query work items share one
+// of q.  Large batches of exactly 8 heads (a TP8 rank's share of 64) take
+// items of two tokens x 8 heads (query_pair_item).  A key work item is 4 tokens.  Key and query work items share one
 // dispatch: the last k_blocks workgroups take key items.
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
@@ -462,6 +462,63 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
     }
 }
 
+// Query work item of two tokens x 8 heads, for calls of exactly 8 heads (a
+// TP8 rank's share of 64): 16 rows in 4 passes, passes 0-1 on token t0 and
+// 2-3 on token t0 + 1, so that an item moves as many bytes as a 16-head item
+// (8-head items of one token left the call 4 % slower; 16-head items of one
+// token left half of each wavefront idle).  Each token has its own position
+// and cos/sin row; row l of the item (token t0 + l / 8, head l % 8) has its
+// gate on lane l, its exponent from pass l / 4, row group l % 4.  A lone last
+// token computes its partner's rows from its own (never stored).
+template <int STYLE, int LAYOUT>
+__device__ __forceinline__ void query_pair_item(const PrepParams& p, int64_t item, int lane) {
+    constexpr int kPasses = 4;
+    const int g = lane >> 4;
+    const int j = lane & (kLanesPerRow - 1);
+    const int64_t t0 = item * 2;
+    const bool two = t0 + 1 < p.T;
+    const int64_t t1 = two ? t0 + 1 : t0;
+    auto tok = [&](int ps) -> int64_t { return ps < 2 ? t0 : t1; };
+    auto head = [&](int ps) -> int { return 4 * (ps & 1) + g; };
+
+    const int64_t pos0 = clamp_position(p.q_pos[t0], p.P);
+    const int64_t pos1 = clamp_position(p.q_pos[t1], p.P);
+    const RopeLane rl0 = rope_lane<STYLE, LAYOUT>(p, pos0, lane);
+    const RopeLane rl1 = rope_lane<STYLE, LAYOUT>(p, pos1, lane);
+    uint4 raw[kPasses];
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps)
+        raw[ps] = load_row<LAYOUT>(p.q + tok(ps) * p.q_st + (int64_t)head(ps) * p.q_sh, j);
+    const int64_t gt = lane < 8 ? t0 : t1;
+    uint32_t wbits = 0;
+    if (lane < 16) wbits = p.w[gt * p.w_st + (lane & 7)];
+
+    int e[kPasses];
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+        float y[8];
+        rope_packed_row<STYLE, LAYOUT>(raw[ps], y, ps < 2 ? rl0 : rl1);
+        e[ps] = scale_exponent(row_max_bits(lane_amax_bits(y)));
+        const uint2 codes = encode8(y, exp2_int(e[ps]));
+        if (ps < 2 || two) store_row<LAYOUT>(p.q_fp8 + (tok(ps) * p.H + head(ps)) * kRow, j, codes);
+    }
+
+    const int src_addr = ((lane & 3) << 4) << 2;
+    int el = 0;
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+        const int v = __builtin_amdgcn_ds_bpermute(src_addr, e[ps]);
+        if ((lane >> 2) == ps) el = v;
+    }
+    if (lane < 8 || (lane < 16 && two)) {
+        const int64_t row = gt * p.H + (lane & 7);
+        const float sc = exp2_int(el);
+        const float ws = __uint_as_float(wbits << 16) * p.weight_scale;
+        p.w_out[row] = ws * sc;
+        if (p.q_scale) p.q_scale[row] = sc;
+    }
+}
+
 template <int STYLE, int LAYOUT>
 __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int lane) {
     const int g = lane >> 4;
@@ -563,8 +620,12 @@ __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
             key_item<STYLE, LAYOUT>(p, it, lane);
     } else {
         const int64_t stride = nq * waves;
-        for (int64_t it = qb * waves + wave; it < p.q_items; it += stride)
-            query_item<STYLE, LAYOUT, HPI>(p, it, lane);
+        for (int64_t it = qb * waves + wave; it < p.q_items; it += stride) {
+            if constexpr (HPI == kHeadsPerItemMid)
+                query_pair_item<STYLE, LAYOUT>(p, it, lane);
+            else
+                query_item<STYLE, LAYOUT, HPI>(p, it, lane);
+        }
     }
 }
 
