@@ -215,6 +215,18 @@ void launch_shapes() {
         CHECK(l.p.heads_per_item == 16 && l.p.head_blocks == 4 && l.p.q_items == 1200);
         CHECK(l.p.k_items == 75 && l.p.k_blocks == 19 && l.grid == 300 + 19);
     }
+    // fused, large batch of exactly 8 heads: items of two tokens x 8 heads, key
+    // workgroups not capped
+    {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(4097, 8);
+        dsaidx_k_args k = make_k(4097);
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1);
+        const Launch& l = g_launches[0];
+        CHECK(l.p.heads_per_item == 8 && l.p.head_blocks == 1 && l.p.q_items == 2049);
+        CHECK(l.p.k_items == 1025 && l.p.k_blocks == 257 && l.grid == 513 + 257);
+    }
     // query side alone, interleaved rope, odd head count
     {
         g_launches.clear();
