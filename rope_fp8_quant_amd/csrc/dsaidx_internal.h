@@ -25,7 +25,8 @@ constexpr int kPagedScaleBytes = 4;            // fp32 scale per slot in a paged
 // the others query work items (which ones: see the kernel); either set may be
 // empty.
 struct PrepParams {
-    // query rows: item = (token, block of heads_per_item heads)
+    // query rows: item = (token, block of heads_per_item heads), or for
+    // heads_per_item == kHeadsPerItemMid two tokens x 8 heads
     const uint16_t* q;
     int64_t q_st, q_sh;
     const uint16_t* w;
@@ -36,10 +37,10 @@ struct PrepParams {
     float* q_scale;
     float weight_scale;
     int32_t H;
-    int32_t heads_per_item;  // kHeadsPerItem or kHeadsPerItemSmall
-    int32_t head_blocks;  // ceil(H / heads_per_item)
+    int32_t heads_per_item;  // kHeadsPerItem, kHeadsPerItemSmall or kHeadsPerItemMid
+    int32_t head_blocks;  // ceil(H / heads_per_item); 1 for two-token items
     int32_t k_blocks;
-    int64_t q_items;      // T * head_blocks (0 when the dispatch has no query work)
+    int64_t q_items;      // T * head_blocks, or ceil(T / 2) for two-token items (0: no query work)
     // key rows: item = 4 consecutive tokens
     const uint16_t* k;
     int64_t k_st;
