@@ -217,6 +217,26 @@ def test_head_counts_large_batches(H, style, rope_dim):
     assert np.array_equal(out2["q_fp8"], out["q_fp8"]) and np.array_equal(out2["w_out"], out["w_out"])
 
 
+def test_two_token_items_on_strided_views():
+    """8 heads in a large batch (items of two tokens x 8 heads) with a padded
+    head stride and k / weights as column slices of one [T, 128 + H] buffer:
+    the same bytes as the dense layout."""
+    T, H = 4099, 8
+    wl = W.make(T, H, table_rows=8192, pos_mode="contiguous", pos_lo=3000, num_slots=T + 5,
+                slot_mode="perm_prefix", seed=808)
+    dense = DeviceCase(wl)
+    dense.run("fused")
+    strided = DeviceCase(wl, q_head_pad=24, gemm_layout=True, cache_row_pad=16)
+    strided.run("fused")
+    a, b = dense.host(), strided.host()
+    assert np.array_equal(a["q_fp8"], b["q_fp8"]) and np.array_equal(a["w_out"], b["w_out"])
+    assert np.array_equal(a["q_scale"], b["q_scale"])
+    assert np.array_equal(a["k_cache"], b["k_cache"][:, :128])
+    rep = {}
+    check_q(a, wl, rep)
+    check_k(a, wl, rep)
+
+
 @pytest.mark.parametrize("style", [W.NEOX, W.INTERLEAVED])
 @pytest.mark.parametrize("rope_dim", [16, 32, 48, 64, 80, 96, 112, 128])
 def test_rope_dims(rope_dim, style):
