@@ -250,10 +250,14 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     const int64_t qb = capped_grid(p.q_items, kBlock);
     int64_t kb = ceil_div(p.k_items, kBlock / 64);
     // key rows are a small share of the bytes at 16 heads per item (a 16th of
-    // the query workgroups suffice); with 8 heads per token they are a sixth
-    const int64_t kcap = p.heads_per_item == dsaidx::kHeadsPerItemMid
-                             ? capped_grid(p.k_items, kBlock) : ceil_div(qb, kKeyBlockDivisor);
+    // the query workgroups suffice); with 8 heads per token they are a sixth,
+    // and a small call is latency-bound: no cap there
+    const int64_t kcap = p.heads_per_item == dsaidx::kHeadsPerItem
+                             ? ceil_div(qb, kKeyBlockDivisor) : capped_grid(p.k_items, kBlock);
     if (kb > kcap) kb = kcap;
+    // small calls of 32 tokens or more: key workgroups first (the kernel's KF)
+    p.k_first = (p.heads_per_item == dsaidx::kHeadsPerItemSmall && p.T >= 32) ? 1 : 0;
+
     p.k_blocks = (int32_t)kb;
     return launch(p, rope->style, qb + kb, kBlock, stream);
 }

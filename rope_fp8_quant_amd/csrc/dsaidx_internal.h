@@ -40,6 +40,7 @@ struct PrepParams {
     int32_t heads_per_item;  // kHeadsPerItem, kHeadsPerItemSmall or kHeadsPerItemMid
     int32_t head_blocks;  // ceil(H / heads_per_item); 1 for two-token items
     int32_t k_blocks;
+    int32_t k_first;      // host only: fused small call with key workgroups first
     int64_t q_items;      // T * head_blocks, or ceil(T / 2) for two-token items (0: no query work)
     // key rows: item = 4 consecutive tokens
     const uint16_t* k;

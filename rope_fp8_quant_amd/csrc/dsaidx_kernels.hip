@@ -595,7 +595,7 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
     }
 }
 
-template <int STYLE, int LAYOUT, int HPI>
+template <int STYLE, int LAYOUT, int HPI, bool KF>
 __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -608,8 +608,12 @@ __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     const bool is_key = (b + 1) * p.k_blocks / nblocks > k_before;
     const int64_t kb = k_before, qb = b - k_before;
 #elif DSAIDX_K_PLACEMENT == 1
-    const bool is_key = b >= nq;
-    const int64_t kb = b - nq, qb = b;
+    // key workgroups last (their LayerNorm work overlaps the query stream's
+    // tail), or first (KF) in small calls of 32 tokens or more, where the key
+    // rows' longer chain of dependent steps is the critical path (64 tokens:
+    // 2.46 against 2.57 us per call; with fewer tokens the query rows are)
+    const bool is_key = KF ? b < p.k_blocks : b >= nq;
+    const int64_t kb = KF ? b : b - nq, qb = KF ? b - p.k_blocks : b;
 #else
     const bool is_key = b < p.k_blocks;
     const int64_t kb = b, qb = b - p.k_blocks;
@@ -662,24 +666,29 @@ hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned b
     PrepParams copy = p;
     void* args[] = {&copy};
     const int hpi = p.heads_per_item;
-    auto pick = [hpi](auto k4, auto k8, auto k16) -> const void* {
-        return hpi == kHeadsPerItemSmall ? reinterpret_cast<const void*>(k4)
+    const bool kf = p.k_first != 0 && hpi == kHeadsPerItemSmall;
+    auto pick = [hpi, kf](auto k4f, auto k4, auto k8, auto k16) -> const void* {
+        return hpi == kHeadsPerItemSmall ? (kf ? reinterpret_cast<const void*>(k4f)
+                                               : reinterpret_cast<const void*>(k4))
                : hpi == kHeadsPerItemMid ? reinterpret_cast<const void*>(k8)
                                          : reinterpret_cast<const void*>(k16);
     };
     const void* fn;
     if (style == 1)
-        fn = pick(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall>,
-                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid>,
-                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem>);
+        fn = pick(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, true>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, false>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid, false>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem, false>);
     else if (p.R <= 64)
-        fn = pick(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall>,
-                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemMid>,
-                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem>);
+        fn = pick(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall, true>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall, false>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemMid, false>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem, false>);
     else
-        fn = pick(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall>,
-                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemMid>,
-                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItem>);
+        fn = pick(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall, true>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall, false>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemMid, false>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItem, false>);
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream);
 }
 

@@ -203,6 +203,16 @@ void launch_shapes() {
         CHECK(l.p.k_items == 2 && l.p.k_blocks == 1 && l.grid == 20 + 1);
         CHECK(l.p.T == 5 && l.p.H == 64 && l.p.R == 64 && l.p.P == 4096 && l.p.rs == 32);
         CHECK(l.p.page_size == 0 && l.p.S == 4096 && l.p.eps == 1e-6f && l.p.q_scale == nullptr);
+        CHECK(l.p.k_first == 0);                 // fewer than 32 tokens: key workgroups last
+    }
+    // fused, small batch of 64 tokens: key workgroups first, none capped
+    {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(64, 64);
+        dsaidx_k_args k = make_k(64);
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        const Launch& l = g_launches[0];
+        CHECK(l.p.heads_per_item == 4 && l.p.k_first == 1 && l.p.k_blocks == 4 && l.grid == 256 + 4);
     }
     // fused, large batch: 16-head items; key workgroups capped at 1/16 of the query ones
     {
@@ -214,6 +224,7 @@ void launch_shapes() {
         const Launch& l = g_launches[0];
         CHECK(l.p.heads_per_item == 16 && l.p.head_blocks == 4 && l.p.q_items == 1200);
         CHECK(l.p.k_items == 75 && l.p.k_blocks == 19 && l.grid == 300 + 19);
+        CHECK(l.p.k_first == 0);
     }
     // fused, large batch of exactly 8 heads: items of two tokens x 8 heads, key
     // workgroups not capped
