@@ -44,10 +44,15 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the prep kernel's sources with comments and blank space
+    removed, so that a comment edit does not void the recorded counters."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -27,9 +27,10 @@
 // its latency (64 tokens x 64 heads: 2.6 us against 3.0 us per call), while
 // for large batches 16-head items move fewer cos/sin rows and gates per byte
 // of q.  Large batches of exactly 8 heads (a TP8 rank's share of 64) take
-// items of two tokens x 8 heads (query_pair_item).  A key work item is 4 tokens.  Key and query work items share one
-// dispatch: the last k_blocks workgroups take key items (the first ones in
-// small calls of 32 tokens or more: template flag KF).
+// items of two tokens x 8 heads (query_pair_item).  A key work item is 4
+// tokens.  Key and query work items share one dispatch: the last k_blocks
+// workgroups take key items (the first ones in small calls of 32 tokens or
+// more: template flag KF).
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
 // is rounded on its own (contraction is off), the LayerNorm sums are fp64, and
