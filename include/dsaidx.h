@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DSAIDX_ABI_VERSION 4
+#define DSAIDX_ABI_VERSION 5
 #define DSAIDX_HEAD_DIM 128 /* width of every head vector and K row */
 
 typedef struct ihipStream_t* dsaidx_stream_t; /* the same type as hipStream_t */
@@ -140,11 +140,25 @@ typedef struct dsaidx_q_args {
 
 /* dsaidx_k_args.flags bits.
  *
- * DSAIDX_K_BF16_INTERMEDIATE: the other K-cache writer of [sglang-fuse]
- *   Accuracy -- the LayerNorm output and the RoPE output are each rounded to
- *   bf16 (nearest, ties to even) before quantisation, instead of going
- *   fp32 -> fp8 in one step.  Codes then differ from the default writer only
- *   near fp8 midpoints (and where the rotation cancels); scales normally agree.
+ * [sglang-fuse] Accuracy compares the fused K-cache writer (fp32 -> fp8 in one
+ * step, the default here) with the unfused one, which rounds to bf16 before
+ * quantising; the page does not say at which points.  Two readings:
+ *
+ * DSAIDX_K_BF16_ROUND_ONCE: the finished fp32 LayerNorm + RoPE value is
+ *   rounded to bf16 (nearest, ties to even) once, just before quantisation.
+ *   A bf16 rounding moves a value by at most 2^-9 of itself, less than half an
+ *   fp8 step, so codes differ from the default writer by at most one step
+ *   wherever the two scales agree; the scale drops one step only on a row
+ *   whose fp32 max lies just above 448 * 2^e and rounds onto it.  This is
+ *   the reading under which the page's observation (identical scales, codes
+ *   one step apart, the fused writer closer to fp32) holds by construction.
+ *
+ * DSAIDX_K_BF16_INTERMEDIATE: the LayerNorm output and the RoPE output are
+ *   each rounded to bf16 (the two kernel boundaries of the unfused chain).
+ *   The rounding of the rotation's inputs can move a value by more than one
+ *   fp8 step where the rotation cancels (a*c close to b*s).
+ *
+ * At most one of the two bf16 bits may be set.
  *
  * DSAIDX_K_PAGED_CACHE: the page-interleaved index-K cache ([sglang-fuse]
  *   Checklist tests two paged layouts without defining them; this is the
@@ -156,6 +170,7 @@ typedef struct dsaidx_q_args {
  *   (k_scale may be NULL). */
 #define DSAIDX_K_BF16_INTERMEDIATE 0x1
 #define DSAIDX_K_PAGED_CACHE 0x2
+#define DSAIDX_K_BF16_ROUND_ONCE 0x4
 
 /* Key side ([sglang-fuse] Motivation and Modifications: fp32 LayerNorm with
  * fp32 params, the index-K cache write at the sliced out_cache_loc).
@@ -164,7 +179,8 @@ typedef struct dsaidx_q_args {
  *                      wider GEMM output is allowed)
  *   ln_gamma, ln_beta  fp32 [128], 16-byte aligned
  *   ln_eps             > 0, finite
- *   flags              0, or DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_PAGED_CACHE bits
+ *   flags              0, or DSAIDX_K_PAGED_CACHE and at most one of
+ *                      DSAIDX_K_BF16_INTERMEDIATE, DSAIDX_K_BF16_ROUND_ONCE
  *   positions          int64 [T], 8-byte aligned
  *   out_cache_loc      int64 [T] slot per token, 8-byte aligned
  *   num_tokens         T >= 0
@@ -308,12 +324,36 @@ typedef struct dsaidx_logits_args {
 dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* args, dsaidx_stream_t stream);
 
 /* Encode n fp32 values to E4M3FN bytes with the device conversion every
- * kernel above uses (round to nearest even), so the conversion can be checked
- * on its own against the format definition.  in: device fp32 [n], 4-byte
- * aligned, every value in [-448, 448] (values outside are outside the
- * contract); out: device bytes [n], 8-byte aligned; n >= 0.  One dispatch. */
+ * kernel above uses, so the conversion can be checked on its own against the
+ * format definition: out[i] = E4M3FN(in[i] / 2^scale_exp), rounded to nearest
+ * even, the division by the power of two exact -- the same call the kernels
+ * make with a row's ue8m0 scale.  in: device fp32 [n], 4-byte aligned, every
+ * in[i] / 2^scale_exp in [-448, 448] (values outside are outside the
+ * contract); out: device bytes [n], 8-byte aligned; n >= 0; scale_exp in
+ * [-126, 127] (2^scale_exp a normal fp32).  One dispatch. */
 dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,
-                                         dsaidx_stream_t stream);
+                                         int32_t scale_exp, dsaidx_stream_t stream);
+
+/* Reference HBM streams: a measurement helper, not part of the indexer path.
+ * Plain kernels with the preparation kernel's access pattern (16-byte
+ * nontemporal loads and stores by every lane, a one-shot grid of 256-thread
+ * workgroups) that give the bandwidth a copy, a pure read and a pure write of
+ * `bytes` reach on this device, so that a kernel's achieved bandwidth can be
+ * set against what its own mix of reads and writes can reach, beside the
+ * published peak.
+ *   mode   DSAIDX_HBM_COPY: dst[0, bytes) = src[0, bytes)
+ *          DSAIDX_HBM_READ: reads src[0, bytes); dst is a sink of at least 16
+ *            bytes that is written only if the data fold to `word` (an XOR of
+ *            all 32-bit words per thread), so pass a `word` they cannot fold to
+ *          DSAIDX_HBM_WRITE: dst[0, bytes) = `word` repeated; src unused
+ *   src, dst  device, 16-byte aligned, not overlapping
+ *   bytes  >= 0, a multiple of 16, at most 2^38
+ * One dispatch (none for bytes == 0). */
+#define DSAIDX_HBM_COPY 0
+#define DSAIDX_HBM_READ 1
+#define DSAIDX_HBM_WRITE 2
+dsaidx_status dsaidx_hbm_stream(int32_t mode, const void* src, void* dst, int64_t bytes,
+                                uint32_t word, dsaidx_stream_t stream);
 
 /* 1 if `device` is a gfx950 GPU this library has code for, else 0 (also when
  * no GPU or HIP runtime is present).  The counterpart of the import-time

@@ -19,7 +19,10 @@
  *     cache write), Modifications (fp32 norm params; the sliced out_cache_loc).
  *   bf16_mode reproduces the other K-cache writer of [sglang-fuse] Accuracy
  *     (rounds to bf16 before quantising, where the fused one goes fp32 -> fp8
- *     in one step).
+ *     in one step).  Two readings of where it rounds: mode 1 at both kernel
+ *     boundaries of the unfused chain (after LayerNorm, after RoPE); mode 2
+ *     once, on the finished fp32 LayerNorm + RoPE value, just before the
+ *     quantisation.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of the repository):
@@ -292,10 +295,10 @@ int oracle_k_values(const uint16_t* k, int64_t k_st,
         float x[ROW], n[ROW];
         for (int i = 0; i < ROW; i++) x[i] = bf16_to_f32(k[t * k_st + i]);
         layernorm_row(x, gamma, beta, eps, n);
-        if (bf16_mode)
+        if (bf16_mode == 1) /* the LayerNorm kernel's bf16 output */
             for (int i = 0; i < ROW; i++) n[i] = round_to_bf16(n[i]);
         rope_row(n, cos_t + p * rs, sin_t + p * rs, R, style);
-        if (bf16_mode)
+        if (bf16_mode == 1 || bf16_mode == 2) /* bf16 handed to the quantiser */
             for (int i = 0; i < ROW; i++) n[i] = round_to_bf16(n[i]);
         memcpy(y + t * ROW, n, sizeof n);
         e[t] = row_exponent(n);

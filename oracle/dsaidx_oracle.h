@@ -64,8 +64,11 @@ int oracle_q_values(const uint16_t* q, int64_t q_st, int64_t q_sh,
 /* K side, values only: for each token t the 128 fp32 values after LayerNorm
  * and RoPE (y[t*128 + i]) and the ue8m0 exponent of the row (e[t]).
  * bf16_mode = 0: fp32 throughout (one fp32 -> fp8 step).
- * bf16_mode = 1: the unfused writer — round to bf16 after LayerNorm and again
- * after RoPE, before quantizing.  Returns 0, or -1 on a bad position. */
+ * bf16_mode = 1: the unfused writer read as rounding to bf16 after LayerNorm
+ * and again after RoPE, before quantizing.
+ * bf16_mode = 2: the unfused writer read as one bf16 rounding of the finished
+ * fp32 LayerNorm + RoPE value, just before quantizing.
+ * Returns 0, or -1 on a bad position. */
 int oracle_k_values(const uint16_t* k, int64_t k_st,
                     const float* gamma, const float* beta, float eps,
                     const int64_t* pos, int64_t T,

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     DSAIDX_ERR_INVALID_ARGUMENT,
     DSAIDX_ERR_UNSUPPORTED,
     DSAIDX_K_BF16_INTERMEDIATE,
+    DSAIDX_K_BF16_ROUND_ONCE,
     DSAIDX_K_PAGED_CACHE,
     DSAIDX_OK,
     DSAIDX_ROPE_INTERLEAVED,

@@ -23,11 +23,13 @@ DSAIDX_ROPE_NEOX = 0
 DSAIDX_ROPE_INTERLEAVED = 1
 DSAIDX_K_BF16_INTERMEDIATE = 0x1
 DSAIDX_K_PAGED_CACHE = 0x2
+DSAIDX_K_BF16_ROUND_ONCE = 0x4
 PAGED_SLOT_BYTES = ROW + 4   # one code row and one fp32 scale per slot
 EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaidx_qk_fused",
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
             "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest",
-            "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes", "dsaidx_mqa_logits")
+            "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes", "dsaidx_mqa_logits",
+            "dsaidx_hbm_stream")
 
 
 class DsaidxError(RuntimeError):
@@ -102,8 +104,10 @@ def lib() -> ctypes.CDLL:
         L.dsaidx_topk_per_row.restype = ctypes.c_int
         L.dsaidx_topk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
         L.dsaidx_topk_workspace_bytes.restype = ctypes.c_int64
-        L.dsaidx_fp8_encode_selftest.argtypes = [P, P, ctypes.c_int64, P]
+        L.dsaidx_fp8_encode_selftest.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
         L.dsaidx_fp8_encode_selftest.restype = ctypes.c_int
+        L.dsaidx_hbm_stream.argtypes = [ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_uint32, P]
+        L.dsaidx_hbm_stream.restype = ctypes.c_int
         L.dsaidx_device_supported.argtypes = [ctypes.c_int]
         L.dsaidx_device_supported.restype = ctypes.c_int
         L.dsaidx_status_string.argtypes = [ctypes.c_int]
@@ -174,13 +178,15 @@ def dsaidx_k_only_prepare_store(k: DsaidxKArgs, rope: DsaidxRope, stream=None) -
                                              _stream_handle(stream)), "dsaidx_k_only_prepare_store")
 
 
-def dsaidx_fp8_encode_selftest(inp, out, stream=None) -> None:
-    """inp: float32 device tensor (contiguous, values in [-448, 448]); out: 1-byte
-    device tensor with as many elements."""
+def dsaidx_fp8_encode_selftest(inp, out, scale_exp: int = 0, stream=None) -> None:
+    """out = E4M3FN(inp / 2^scale_exp) with the kernels' device conversion.
+    inp: float32 device tensor (contiguous, inp / 2^scale_exp in [-448, 448]);
+    out: 1-byte device tensor with as many elements."""
+    _on_device(inp=inp, out=out)
     _need(inp.is_contiguous() and out.is_contiguous() and inp.numel() == out.numel()
           and out.element_size() == 1, "contiguous float32 input and 1-byte output of equal size")
     _check(lib().dsaidx_fp8_encode_selftest(ctypes.c_void_p(_ptr(inp)), ctypes.c_void_p(_ptr(out)),
-                                            inp.numel(), _stream_handle(stream)),
+                                            inp.numel(), int(scale_exp), _stream_handle(stream)),
            "dsaidx_fp8_encode_selftest")
 
 
@@ -200,6 +206,7 @@ def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None, workspac
     allocated here when that size is not 0 (keep one to reuse, e.g. under graph
     capture)."""
     import torch
+    _on_device(logits=logits, out=out, lengths=lengths, workspace=workspace)
     _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
           "logits must be float32 [rows, cols] with unit column stride")
     rows, cols = logits.shape
@@ -223,6 +230,28 @@ def dsaidx_topk_per_row(logits, k: int, out, lengths=None, stream=None, workspac
            "dsaidx_topk_per_row")
 
 
+DSAIDX_HBM_COPY = 0
+DSAIDX_HBM_READ = 1
+DSAIDX_HBM_WRITE = 2
+
+
+def dsaidx_hbm_stream(mode: int, src, dst, nbytes: int, word: int = 0, stream=None) -> None:
+    """Reference HBM stream (a measurement helper): copy, read or write nbytes
+    with the preparation kernel's access pattern.  src / dst: contiguous
+    device tensors of at least nbytes (dst at least 16 bytes for a read)."""
+    _on_device(src=src, dst=dst)
+    for t in (src, dst):
+        if t is not None:
+            _need(t.is_contiguous(), "src / dst must be contiguous")
+    if mode != DSAIDX_HBM_WRITE:
+        _need(src is not None and src.numel() * src.element_size() >= nbytes, "src too small")
+    need_dst = 16 if mode == DSAIDX_HBM_READ else nbytes
+    _need(dst is not None and dst.numel() * dst.element_size() >= need_dst, "dst too small")
+    _check(lib().dsaidx_hbm_stream(int(mode), ctypes.c_void_p(_ptr(src)), ctypes.c_void_p(_ptr(dst)),
+                                   int(nbytes), int(word) & 0xFFFFFFFF, _stream_handle(stream)),
+           "dsaidx_hbm_stream")
+
+
 def dsaidx_mqa_logits(args: DsaidxLogitsArgs, stream=None) -> None:
     _check(lib().dsaidx_mqa_logits(ctypes.byref(args), _stream_handle(stream)), "dsaidx_mqa_logits")
 
@@ -238,10 +267,25 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _on_device(**tensors):
+    """Every given tensor (None skipped) lives on the current GPU.  The library
+    takes plain device pointers and never reads them on the host, so a host
+    tensor or one on another device must be refused here, before any launch."""
+    import torch
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _need(isinstance(t, torch.Tensor) and t.is_cuda, "%s must be a GPU tensor" % name)
+        _need(t.device.index == torch.cuda.current_device(),
+              "%s is on cuda:%d, not on the current device cuda:%d"
+              % (name, t.device.index, torch.cuda.current_device()))
+
+
 def rope_args(cos, sin, rope_dim: int = 64, style: int = DSAIDX_ROPE_NEOX) -> DsaidxRope:
     """cos, sin: float32 [P, >= rope_dim/2] views with unit column stride and
     a common row stride (e.g. the two halves of one [P, rope_dim] cache)."""
     import torch
+    _on_device(cos=cos, sin=sin)
     _need(cos.dtype == torch.float32 and sin.dtype == torch.float32, "cos/sin must be float32")
     _need(cos.dim() == 2 and sin.dim() == 2 and cos.shape[0] == sin.shape[0], "cos/sin [P, n]")
     _need(cos.stride(1) == 1 and sin.stride(1) == 1 and cos.stride(0) == sin.stride(0),
@@ -256,6 +300,8 @@ def q_args(q, weights, positions, q_fp8, weights_out, q_scale_out=None,
     [T, H, 128] contiguous; weights_out (and q_scale_out) float32 [T, H]
     contiguous."""
     import torch
+    _on_device(q=q, weights=weights, positions=positions, q_fp8=q_fp8, weights_out=weights_out,
+               q_scale_out=q_scale_out)
     _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == ROW and q.stride(2) == 1,
           "q must be bf16 [T, H, 128] with unit inner stride")
     T, H = q.shape[0], q.shape[1]
@@ -283,9 +329,12 @@ def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cach
     codes go to the first 128 bytes of each row), k_scale float32 [S].
     Paged cache (flags has DSAIDX_K_PAGED_CACHE): k_cache a contiguous 1-byte
     tensor of num_slots * 132 bytes holding pages of page_size slots (code
-    rows, then fp32 scales); k_scale unused.  DSAIDX_K_BF16_INTERMEDIATE
-    selects the bf16-intermediate writer."""
+    rows, then fp32 scales); k_scale unused.  DSAIDX_K_BF16_ROUND_ONCE or
+    DSAIDX_K_BF16_INTERMEDIATE selects one of the two readings of the unfused
+    (bf16) K-cache writer."""
     import torch
+    _on_device(k=k, ln_gamma=ln_gamma, ln_beta=ln_beta, positions=positions,
+               out_cache_loc=out_cache_loc, k_cache=k_cache, k_scale=k_scale)
     _need(k.dtype == torch.bfloat16 and k.dim() == 2 and k.shape[1] == ROW and k.stride(1) == 1,
           "k must be bf16 [T, 128] with unit inner stride")
     T = k.shape[0]
@@ -320,6 +369,8 @@ def logits_args(q_fp8, weights, k_cache, logits, k_scale=None, key_slots=None, l
     key_slots: int32 [N] or None (key s is slot s); lengths: int32 [T] or
     None.  The cache arguments are those of k_args (read only)."""
     import torch
+    _on_device(q_fp8=q_fp8, weights=weights, k_cache=k_cache, logits=logits, k_scale=k_scale,
+               key_slots=key_slots, lengths=lengths)
     _need(q_fp8.element_size() == 1 and q_fp8.dim() == 3 and q_fp8.shape[2] == ROW
           and q_fp8.is_contiguous(), "q_fp8 must be a contiguous 1-byte [T, H, 128] tensor")
     T, H = q_fp8.shape[0], q_fp8.shape[1]

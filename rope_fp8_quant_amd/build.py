@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libdsaidx.so")
 ARCH = "gfx950"
 
-SOURCES = ["dsaidx_kernels.hip", "dsaidx_topk.hip", "dsaidx_logits.hip", "dsaidx_api.cpp"]
+SOURCES = ["dsaidx_kernels.hip", "dsaidx_topk.hip", "dsaidx_logits.hip", "dsaidx_hbm_ref.hip",
+           "dsaidx_api.cpp"]
 HEADERS = [os.path.join(INCLUDE, "dsaidx.h"), os.path.join(CSRC, "dsaidx_internal.h")]
 
 

@@ -9,6 +9,7 @@
 
 static_assert(dsaidx::kKeyBf16Intermediate == DSAIDX_K_BF16_INTERMEDIATE, "flag bits");
 static_assert(dsaidx::kKeyPagedCache == DSAIDX_K_PAGED_CACHE, "flag bits");
+static_assert(dsaidx::kKeyBf16Once == DSAIDX_K_BF16_ROUND_ONCE, "flag bits");
 
 namespace {
 
@@ -21,10 +22,17 @@ constexpr unsigned kSmallBlock = 64;      // 1 wavefront (k-only launch shape)
 // Launch shape: one workgroup per 4 work items up to this many workgroups
 // (beyond it the kernels loop).  A one-shot grid streams measurably faster on
 // MI355X than a grid capped near the CU count with long grid-stride loops.
+// A dispatch counts its work-items in 32 bits, so workgroups * block size
+// stays below 2^32 (max_grid).
 #ifndef DSAIDX_MAX_GRID
 #define DSAIDX_MAX_GRID (1 << 24)
 #endif
 constexpr int64_t kMaxGrid = DSAIDX_MAX_GRID;
+
+int64_t max_grid(unsigned block) {
+    const int64_t fit = ((int64_t(1) << 32) - 1) / block;
+    return fit < kMaxGrid ? fit : kMaxGrid;
+}
 constexpr int kKeyBlockDivisor = 16;      // fused: key workgroups <= query workgroups / 16
 
 bool token_count_ok(int64_t t) { return t >= 0 && t <= kMaxTokens; }
@@ -68,7 +76,9 @@ dsaidx_status check_k(const dsaidx_k_args* k) {
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (k->k_stride_t < dsaidx::kRow || k->k_stride_t % 8 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (!(k->ln_eps > 0.0f) || !std::isfinite(k->ln_eps)) return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (k->flags & ~(DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_PAGED_CACHE))
+    if (k->flags & ~(DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_ROUND_ONCE))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if ((k->flags & DSAIDX_K_BF16_INTERMEDIATE) && (k->flags & DSAIDX_K_BF16_ROUND_ONCE))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (k->num_slots < 1) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (k->flags & DSAIDX_K_PAGED_CACHE) {
@@ -177,7 +187,7 @@ int64_t logits_key_chunk(int64_t T, int64_t N, int64_t* chunks) {
 
 int64_t capped_grid(int64_t items, unsigned block) {
     const int64_t need = ceil_div(items, block / 64);
-    return need < kMaxGrid ? need : kMaxGrid;
+    return need < max_grid(block) ? need : max_grid(block);
 }
 
 }  // namespace
@@ -355,14 +365,28 @@ dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t str
 }
 
 dsaidx_status dsaidx_fp8_encode_selftest(const float* in, uint8_t* out, int64_t n,
-                                         dsaidx_stream_t stream) {
+                                         int32_t scale_exp, dsaidx_stream_t stream) {
     if (n < 0 || !in || !out || !aligned(in, 4) || !aligned(out, 8))
         return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (scale_exp < -126 || scale_exp > 127) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (n == 0) return DSAIDX_OK;
     int64_t grid = ceil_div(ceil_div(n, 8), 256);
-    if (grid > kMaxGrid) grid = kMaxGrid;
-    return to_status(dsaidx::launch_fp8_selftest(in, out, n, (unsigned)grid,
+    if (grid > max_grid(256)) grid = max_grid(256);
+    return to_status(dsaidx::launch_fp8_selftest(in, out, n, std::ldexp(1.0f, scale_exp),
+                                                 (unsigned)grid,
                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+dsaidx_status dsaidx_hbm_stream(int32_t mode, const void* src, void* dst, int64_t bytes,
+                                uint32_t word, dsaidx_stream_t stream) {
+    if (mode != DSAIDX_HBM_COPY && mode != DSAIDX_HBM_READ && mode != DSAIDX_HBM_WRITE)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (bytes < 0 || bytes % 16 != 0 || bytes > (int64_t(1) << 38)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return DSAIDX_OK;
+    if (!dst || !aligned(dst, 16)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (mode != DSAIDX_HBM_WRITE && (!src || !aligned(src, 16))) return DSAIDX_ERR_INVALID_ARGUMENT;
+    return to_status(dsaidx::launch_hbm_stream(mode, src, dst, bytes / 16, word,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int dsaidx_device_supported(int device) {

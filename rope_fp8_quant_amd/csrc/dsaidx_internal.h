@@ -19,6 +19,7 @@ constexpr int64_t kSmallBatchHeadRows = 16384;
 constexpr int kTokensPerKItem = 4;  // key rows per wavefront work item
 constexpr int32_t kKeyBf16Intermediate = 0x1;  // DSAIDX_K_BF16_INTERMEDIATE
 constexpr int32_t kKeyPagedCache = 0x2;        // DSAIDX_K_PAGED_CACHE
+constexpr int32_t kKeyBf16Once = 0x4;          // DSAIDX_K_BF16_ROUND_ONCE
 constexpr int kPagedScaleBytes = 4;            // fp32 scale per slot in a paged cache
 
 // Everything one dispatch needs.  k_blocks workgroups run key work items and
@@ -81,9 +82,15 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
                        int64_t rows, int64_t cols, int32_t k, int32_t* out, void* workspace,
                        hipStream_t stream);
 
-// Enqueue the stand-alone E4M3FN conversion (self-test of the device encoder).
-hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigned grid,
-                               hipStream_t stream);
+// Enqueue the stand-alone E4M3FN conversion of in[i] / scale (self-test of
+// the device encoder; scale a power of two).
+hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, float scale,
+                               unsigned grid, hipStream_t stream);
+
+// Reference HBM stream over `vectors` 16-byte vectors: mode 0 copy, 1 read,
+// 2 write (one dispatch).
+hipError_t launch_hbm_stream(int mode, const void* src, void* dst, int64_t vectors,
+                             uint32_t word, hipStream_t stream);
 
 // Index logits (one dispatch): queries of at most kLogitsMaxHeads heads
 // against num_keys keys of the index-K cache.

@@ -566,15 +566,16 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
         n[m] = dg + bet[m];
     }
 
-    // The bf16-intermediate writer rounds the LayerNorm output and the RoPE
-    // output to bf16 ([sglang-fuse] Accuracy, the unfused K-cache writer).
+    // The unfused K-cache writer of [sglang-fuse] Accuracy rounds to bf16
+    // before quantising: at both kernel boundaries (LayerNorm output and RoPE
+    // output) or once, on the finished value, depending on the flag.
     const bool bf16_steps = (p.k_flags & kKeyBf16Intermediate) != 0;
     if (bf16_steps) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) n[m] = round_bf16(n[m]);
     }
     rope_row<STYLE, LAYOUT>(n, rl);
-    if (bf16_steps) {
+    if (bf16_steps || (p.k_flags & kKeyBf16Once) != 0) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) n[m] = round_bf16(n[m]);
     }
@@ -635,16 +636,17 @@ __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     }
 }
 
-// Eight consecutive values per lane through the kernels' encoder (scale 1).
+// Eight consecutive values per lane through the kernels' encoder, with a
+// power-of-two scale as a row's ue8m0 scale is passed.
 __global__ __launch_bounds__(256) void fp8_encode_selftest_kernel(const float* in, uint8_t* out,
-                                                                  int64_t n) {
+                                                                  int64_t n, float scale) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
     for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; base < n;
          base += stride) {
         float v[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) v[m] = base + m < n ? in[base + m] : 0.0f;
-        const uint2 c = encode8(v, 1.0f);
+        const uint2 c = encode8(v, scale);
         if (base + 8 <= n) {
             *reinterpret_cast<uint2*>(out + base) = c;
         } else {
@@ -656,9 +658,9 @@ __global__ __launch_bounds__(256) void fp8_encode_selftest_kernel(const float* i
 
 }  // namespace
 
-hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, unsigned grid,
-                               hipStream_t stream) {
-    void* args[] = {&in, &out, &n};
+hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, float scale,
+                               unsigned grid, hipStream_t stream) {
+    void* args[] = {&in, &out, &n, &scale};
     return hipLaunchKernel(reinterpret_cast<const void*>(&fp8_encode_selftest_kernel), dim3(grid),
                            dim3(256), args, 0, stream);
 }

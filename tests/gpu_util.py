@@ -132,8 +132,15 @@ def oracle_q(wl: W.Workload, tokens=None):
     return oracle.q_side(q, w, pos, wl.cos, wl.sin, wl.rope_dim, wl.style, wl.weight_scale)
 
 
+def bf16_mode_of(k_flags: int) -> int:
+    """The oracle's bf16_mode for a set of DSAIDX_K_* flags."""
+    if k_flags & R.DSAIDX_K_BF16_INTERMEDIATE:
+        return 1
+    return 2 if k_flags & R.DSAIDX_K_BF16_ROUND_ONCE else 0
+
+
 def oracle_k(wl: W.Workload, cache_row_pad=0, k_flags=0, page_size=0):
-    bf16_mode = 1 if k_flags & R.DSAIDX_K_BF16_INTERMEDIATE else 0
+    bf16_mode = bf16_mode_of(k_flags)
     if k_flags & R.DSAIDX_K_PAGED_CACHE:
         buf = np.full(wl.num_slots * (ROW + 4), SENTINEL, np.uint8)
         oracle.k_side_paged(wl.k, wl.gamma, wl.beta, wl.eps, wl.positions, wl.out_cache_loc,
@@ -206,7 +213,7 @@ def k_rows_near_scale_boundary(wl: W.Workload, k_flags=0) -> int:
     order different from the oracle's could move the ue8m0 exponent.  The
     scales are still compared exactly; this count says how many rows that
     exactness rests on the fp64 sums for."""
-    bf16_mode = 1 if k_flags & R.DSAIDX_K_BF16_INTERMEDIATE else 0
+    bf16_mode = bf16_mode_of(k_flags)
     y, _ = oracle.k_values(wl.k, wl.gamma, wl.beta, wl.eps, wl.positions, wl.cos, wl.sin,
                            wl.rope_dim, wl.style, bf16_mode)
     ag = np.maximum(np.abs(y).max(axis=1), np.float32(1e-4)).astype(np.float32)

@@ -15,7 +15,7 @@
 namespace {
 
 struct Launch {
-    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test, 3 logits
+    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test, 3 logits, 4 HBM stream
     dsaidx::PrepParams p;
     dsaidx::LogitsParams lp;
     int style;
@@ -72,7 +72,8 @@ hipError_t launch_topk(const float*, int64_t row_stride, const int32_t*, int64_t
     return g_fail;
 }
 
-hipError_t launch_fp8_selftest(const float*, uint8_t*, int64_t n, unsigned grid, hipStream_t) {
+hipError_t launch_fp8_selftest(const float*, uint8_t*, int64_t n, float scale, unsigned grid, hipStream_t) {
+    CHECK(scale > 0.0f);
     Launch l;
     std::memset(&l, 0, sizeof l);
     l.kind = 2;
@@ -87,6 +88,16 @@ hipError_t launch_logits(const LogitsParams& p, hipStream_t) {
     std::memset(&l, 0, sizeof l);
     l.kind = 3;
     l.lp = p;
+    g_launches.push_back(l);
+    return g_fail;
+}
+
+hipError_t launch_hbm_stream(int mode, const void*, void*, int64_t vectors, uint32_t, hipStream_t) {
+    Launch l;
+    std::memset(&l, 0, sizeof l);
+    l.kind = 4;
+    l.n = vectors;
+    l.style = mode;
     g_launches.push_back(l);
     return g_fail;
 }
@@ -177,7 +188,7 @@ void expect_rejected(F f, int line) {
 #define REJECT(expr) expect_rejected([&] { return (expr); }, __LINE__)
 
 void abi_and_status() {
-    CHECK(dsaidx_abi_version() == 4);
+    CHECK(dsaidx_abi_version() == DSAIDX_ABI_VERSION);
     const dsaidx_status all[] = {DSAIDX_OK, DSAIDX_ERR_INVALID_ARGUMENT, DSAIDX_ERR_UNSUPPORTED,
                                  DSAIDX_ERR_HIP};
     for (dsaidx_status s : all) {
@@ -273,6 +284,10 @@ void launch_shapes() {
         CHECK(dsaidx_k_norm_rope_quant_store(&k, &rope, nullptr) == DSAIDX_OK);
         CHECK(g_launches.size() == 1 && g_launches[0].p.page_size == 64);
         CHECK(g_launches[0].p.k_flags == (DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_INTERMEDIATE));
+        g_launches.clear();
+        k.flags = DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_ROUND_ONCE;
+        CHECK(dsaidx_k_norm_rope_quant_store(&k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1 && g_launches[0].p.k_flags == (DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_ROUND_ONCE));
     }
     // no tokens: nothing enqueued, from any entry
     {
@@ -387,7 +402,8 @@ void rejected_arguments() {
     bad_k([](dsaidx_k_args& k) { k.ln_eps = -1e-6f; });
     bad_k([](dsaidx_k_args& k) { k.ln_eps = NAN; });
     bad_k([](dsaidx_k_args& k) { k.ln_eps = INFINITY; });
-    bad_k([](dsaidx_k_args& k) { k.flags = 0x4; });
+    bad_k([](dsaidx_k_args& k) { k.flags = 0x8; });
+    bad_k([](dsaidx_k_args& k) { k.flags = DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_BF16_ROUND_ONCE; });
     bad_k([](dsaidx_k_args& k) { k.num_slots = 0; });
     bad_k([](dsaidx_k_args& k) { k.k_cache_row_stride = 120; });
     bad_k([](dsaidx_k_args& k) { k.k_cache_row_stride = 132; });
@@ -437,13 +453,27 @@ void topk_and_selftest() {
     REJECT(dsaidx_topk_per_row(lg, 1000, nullptr, 3, 1000, 10, nullptr, nullptr, 0, nullptr));
     REJECT(dsaidx_topk_per_row(nullptr, 1000, nullptr, 3, 1000, 10, out, nullptr, 0, nullptr));
     g_launches.clear();
-    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 0, nullptr) == DSAIDX_OK);
+    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 0, 0, nullptr) == DSAIDX_OK);
     CHECK(g_launches.empty());
-    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 1000, nullptr) == DSAIDX_OK);
+    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 1000, -22, nullptr) == DSAIDX_OK);
     CHECK(g_launches.size() == 1 && g_launches[0].kind == 2 && g_launches[0].grid == 1);
-    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), -1, nullptr));
-    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32772), 8, nullptr));
-    REJECT(dsaidx_fp8_encode_selftest(nullptr, at<uint8_t>(32768), 8, nullptr));
+    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 1000, -126, nullptr) == DSAIDX_OK);
+    CHECK(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 1000, 127, nullptr) == DSAIDX_OK);
+    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), -1, 0, nullptr));
+    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32772), 8, 0, nullptr));
+    REJECT(dsaidx_fp8_encode_selftest(nullptr, at<uint8_t>(32768), 8, 0, nullptr));
+    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 8, -127, nullptr));
+    REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 8, 128, nullptr));
+    // reference HBM streams: byte count in 16-byte vectors, nothing for 0 bytes
+    g_launches.clear();
+    CHECK(dsaidx_hbm_stream(DSAIDX_HBM_COPY, lg, at<uint8_t>(32768), 0, 0, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.empty());
+    CHECK(dsaidx_hbm_stream(DSAIDX_HBM_READ, lg, at<uint8_t>(32768), 4096, 7, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].kind == 4 && g_launches[0].n == 256 &&
+          g_launches[0].style == DSAIDX_HBM_READ);
+    REJECT(dsaidx_hbm_stream(DSAIDX_HBM_WRITE, nullptr, at<uint8_t>(32776), 64, 0, nullptr));
+    REJECT(dsaidx_hbm_stream(DSAIDX_HBM_COPY, lg, at<uint8_t>(32768), 40, 0, nullptr));
+    REJECT(dsaidx_hbm_stream(7, lg, at<uint8_t>(32768), 64, 0, nullptr));
 }
 
 }  // namespace

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_struct_sizes(L):
-    assert B.dsaidx_abi_version() == 4
+    assert B.dsaidx_abi_version() == 5
     assert L.dsaidx_struct_size(0) == ctypes.sizeof(B.DsaidxRope) == 40
     assert L.dsaidx_struct_size(1) == ctypes.sizeof(B.DsaidxQArgs) == 88
     assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 104
@@ -159,7 +159,8 @@ BAD_K = [dict(k=None), dict(ln_gamma=None), dict(ln_beta=None), dict(positions=N
          dict(k=FAKE + 8), dict(ln_gamma=FAKE + 4), dict(out_cache_loc=FAKE + 4),
          dict(k_cache=FAKE + 4), dict(k_scale=FAKE + 2), dict(num_tokens=-3),
          dict(k_stride_t=64), dict(k_stride_t=130), dict(ln_eps=0.0), dict(ln_eps=-1e-6),
-         dict(ln_eps=float("nan")), dict(ln_eps=float("inf")), dict(flags=4), dict(flags=-1),
+         dict(ln_eps=float("nan")), dict(ln_eps=float("inf")), dict(flags=8), dict(flags=-1),
+         dict(flags=5), dict(flags=7, page_size=64, num_slots=128),
          dict(k_cache_row_stride=120), dict(k_cache_row_stride=132), dict(num_slots=0),
          dict(flags=1, k_scale=None),
          dict(flags=2, page_size=0), dict(flags=2, page_size=1), dict(flags=2, page_size=3),
@@ -188,12 +189,26 @@ def test_token_count_range(L, T):
 
 
 def test_fp8_selftest_argument_checks(L):
-    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, 0, None) == B.DSAIDX_OK
-    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, -1, None) == 1
-    assert L.dsaidx_fp8_encode_selftest(None, FAKE, 8, None) == 1
-    assert L.dsaidx_fp8_encode_selftest(FAKE, None, 8, None) == 1
-    assert L.dsaidx_fp8_encode_selftest(FAKE + 2, FAKE, 8, None) == 1
-    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE + 4, 8, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, 0, 0, None) == B.DSAIDX_OK
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, -1, 0, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(None, FAKE, 8, 0, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, None, 8, 0, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE + 2, FAKE, 8, 0, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE + 4, 8, 0, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, 8, -127, None) == 1
+    assert L.dsaidx_fp8_encode_selftest(FAKE, FAKE, 8, 128, None) == 1
+
+
+def test_hbm_stream_argument_checks(L):
+    f = L.dsaidx_hbm_stream
+    assert f(0, FAKE, FAKE, 0, 0, None) == B.DSAIDX_OK            # nothing to do
+    assert f(2, None, None, 0, 0, None) == B.DSAIDX_OK
+    for bad in [(3, FAKE, FAKE, 64), (-1, FAKE, FAKE, 64), (0, FAKE, FAKE, -16),
+                (0, FAKE, FAKE, 24), (0, FAKE, FAKE, (1 << 38) + 16), (0, None, FAKE, 64),
+                (0, FAKE, None, 64), (1, None, FAKE, 64), (1, FAKE, None, 64), (2, FAKE, None, 64),
+                (0, FAKE + 8, FAKE, 64), (0, FAKE, FAKE + 4, 64), (2, None, FAKE + 8, 64)]:
+        mode, src, dst, n = bad
+        assert f(mode, src, dst, n, 0, None) == B.DSAIDX_ERR_INVALID_ARGUMENT, bad
 
 
 def test_topk_argument_checks(L):
@@ -288,3 +303,26 @@ def test_header_compiles_and_links_as_c99(L, tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.strip() == "DSAIDX_ERR_UNSUPPORTED 0"
+
+
+def test_binding_refuses_host_tensors(L):
+    """The binding hands plain device pointers to the library, which never
+    reads them on the host: every tensor builder and wrapper refuses a host
+    tensor with ValueError before anything is launched."""
+    import torch
+    T, H, S = 2, 4, 8
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    i64 = lambda *s: torch.zeros(s, dtype=torch.int64)
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    cases = [
+        lambda: B.rope_args(f32(16, 32), f32(16, 32)),
+        lambda: B.q_args(bf(T, H, 128), bf(T, H), i64(T), u8(T, H, 128), f32(T, H)),
+        lambda: B.k_args(bf(T, 128), f32(128), f32(128), 1e-6, i64(T), i64(T), u8(S, 128), f32(S)),
+        lambda: B.logits_args(u8(T, H, 128), f32(T, H), u8(S, 128), f32(T, S), k_scale=f32(S)),
+        lambda: B.dsaidx_topk_per_row(f32(T, 64), 4, torch.zeros((T, 4), dtype=torch.int32)),
+        lambda: B.dsaidx_fp8_encode_selftest(f32(64), u8(64)),
+    ]
+    for make in cases:
+        with pytest.raises(ValueError, match="GPU tensor"):
+            make()

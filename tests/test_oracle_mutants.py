@@ -44,6 +44,9 @@ MUTANTS = [
     ("cache_ignores_slot", "encode_row(y + t * ROW, e[t], k_cache + slot * row_stride);",
      "encode_row(y + t * ROW, e[t], k_cache + t * row_stride);"),
     ("bf16_round_half_up", "u += 0x7FFFu + lsb;", "u += 0x8000u + 0 * lsb;"),
+    ("bf16_once_also_before_rope", "if (bf16_mode == 1) /* the LayerNorm kernel's bf16 output */",
+     "if (bf16_mode >= 1) /* the LayerNorm kernel's bf16 output */"),
+    ("bf16_once_skipped", "if (bf16_mode == 1 || bf16_mode == 2)", "if (bf16_mode == 1)"),
     ("paged_scale_offset", "memcpy(page + page_size * ROW + off * (int64_t)sizeof(float), &sc, sizeof sc);",
      "memcpy(page + page_size * ROW + (page_size - 1 - off) * (int64_t)sizeof(float), &sc, sizeof sc);"),
 ]

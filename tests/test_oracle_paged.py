@@ -30,7 +30,7 @@ def planar_then_rearranged(oracle_lib, wl, page, bf16_mode):
     return np.concatenate(pages)
 
 
-@pytest.mark.parametrize("bf16_mode", [0, 1])
+@pytest.mark.parametrize("bf16_mode", [0, 1, 2])
 @pytest.mark.parametrize("page", [2, 16, 64])
 def test_paged_equals_planar_under_the_address_map(oracle_lib, page, bf16_mode):
     wl = W.named(0)
