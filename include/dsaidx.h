@@ -263,6 +263,28 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
                                   void* workspace, int64_t workspace_bytes,
                                   dsaidx_stream_t stream);
 
+/* Top-k per row for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * arguments and result as dsaidx_topk_per_row, without the workspace: a call
+ * that needs one (rows longer than 32768 logits) uses a library-owned device
+ * array of DSAIDX_TOPK_NOALLOC_SCRATCH_BYTES (16 MiB) on the current GPU,
+ * part of the library's code object (each GPU the library runs on holds its
+ * own until the process ends).  The call allocates nothing.
+ *   - A call whose dsaidx_topk_workspace_bytes exceeds that size (e.g. more
+ *     than 227 rows of 131072 logits) returns DSAIDX_ERR_INVALID_ARGUMENT and
+ *     enqueues nothing.
+ *   - `stream` must belong to the current device (else
+ *     DSAIDX_ERR_INVALID_ARGUMENT).  Devices 0..63 are supported.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; the kernels clear what they need, so those contents
+ *     do not matter.  Calls that overlap on one GPU (on different streams, or
+ *     from several host threads) race on the array: order them on one stream.
+ */
+#define DSAIDX_TOPK_NOALLOC_SCRATCH_BYTES ((int64_t)16 << 20)
+dsaidx_status dsaidx_topk_per_row_noalloc(const float* logits, int64_t row_stride,
+                                          const int32_t* lengths, int64_t rows, int64_t cols,
+                                          int32_t k, int32_t* out_idx, dsaidx_stream_t stream);
+
 /* Bytes of workspace dsaidx_topk_per_row needs for this shape: 0 when
  * cols <= 32768, else rows * (8224 + 8 * L) with L = max(4096, cols / 16)
  * rounded up to a multiple of 4 (per row: a 2048-bin histogram and counters,

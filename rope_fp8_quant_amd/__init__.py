@@ -29,6 +29,7 @@ from .binding import (  # noqa: F401
     dsaidx_qk_fused,
     dsaidx_status_string,
     dsaidx_topk_per_row,
+    dsaidx_topk_per_row_noalloc,
     dsaidx_topk_workspace_bytes,
     k_args,
     lib,

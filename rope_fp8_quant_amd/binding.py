@@ -29,7 +29,8 @@ EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaid
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
             "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest",
             "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes", "dsaidx_mqa_logits",
-            "dsaidx_hbm_stream")
+            "dsaidx_hbm_stream", "dsaidx_topk_per_row_noalloc")
+TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class DsaidxError(RuntimeError):
@@ -102,6 +103,9 @@ def lib() -> ctypes.CDLL:
         L.dsaidx_topk_per_row.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int32, P, P, ctypes.c_int64, P]
         L.dsaidx_topk_per_row.restype = ctypes.c_int
+        L.dsaidx_topk_per_row_noalloc.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int32, P, P]
+        L.dsaidx_topk_per_row_noalloc.restype = ctypes.c_int
         L.dsaidx_topk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
         L.dsaidx_topk_workspace_bytes.restype = ctypes.c_int64
         L.dsaidx_fp8_encode_selftest.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
@@ -250,6 +254,28 @@ def dsaidx_hbm_stream(mode: int, src, dst, nbytes: int, word: int = 0, stream=No
     _check(lib().dsaidx_hbm_stream(int(mode), ctypes.c_void_p(_ptr(src)), ctypes.c_void_p(_ptr(dst)),
                                    int(nbytes), int(word) & 0xFFFFFFFF, _stream_handle(stream)),
            "dsaidx_hbm_stream")
+
+
+def dsaidx_topk_per_row_noalloc(logits, k: int, out, lengths=None, stream=None) -> None:
+    """dsaidx_topk_per_row without a workspace argument and without any
+    allocation, here or in the library: rows longer than 32768 logits use the
+    library's own 16 MiB device array (calls on one GPU must be ordered on one
+    stream).  Same tensor rules as dsaidx_topk_per_row."""
+    import torch
+    _on_device(logits=logits, out=out, lengths=lengths)
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
+          "logits must be float32 [rows, cols] with unit column stride")
+    rows, cols = logits.shape
+    _need(out.dtype == torch.int32 and tuple(out.shape) == (rows, k) and out.is_contiguous(),
+          "out must be contiguous int32 [rows, k]")
+    if lengths is not None:
+        _need(lengths.dtype == torch.int32 and lengths.numel() == rows and lengths.is_contiguous(),
+              "lengths must be contiguous int32 [rows]")
+    _check(lib().dsaidx_topk_per_row_noalloc(ctypes.c_void_p(_ptr(logits)),
+                                             logits.stride(0) if rows else cols,
+                                             ctypes.c_void_p(_ptr(lengths)), rows, cols, int(k),
+                                             ctypes.c_void_p(_ptr(out)), _stream_handle(stream)),
+           "dsaidx_topk_per_row_noalloc")
 
 
 def dsaidx_mqa_logits(args: DsaidxLogitsArgs, stream=None) -> None:

@@ -10,6 +10,7 @@
 static_assert(dsaidx::kKeyBf16Intermediate == DSAIDX_K_BF16_INTERMEDIATE, "flag bits");
 static_assert(dsaidx::kKeyPagedCache == DSAIDX_K_PAGED_CACHE, "flag bits");
 static_assert(dsaidx::kKeyBf16Once == DSAIDX_K_BF16_ROUND_ONCE, "flag bits");
+static_assert(dsaidx::kTopkScratchBytes == DSAIDX_TOPK_NOALLOC_SCRATCH_BYTES, "scratch size");
 
 namespace {
 
@@ -298,6 +299,30 @@ dsaidx_status dsaidx_topk_per_row(const float* logits, int64_t row_stride, const
         return DSAIDX_ERR_INVALID_ARGUMENT;
     return to_status(dsaidx::launch_topk(logits, row_stride, lengths, rows, cols, k, out_idx,
                                          workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+dsaidx_status dsaidx_topk_per_row_noalloc(const float* logits, int64_t row_stride,
+                                          const int32_t* lengths, int64_t rows, int64_t cols,
+                                          int32_t k, int32_t* out_idx, dsaidx_stream_t stream) {
+    if (!topk_shape_ok(rows, cols, k)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    const int64_t need = dsaidx::topk_workspace_bytes(rows, cols, k);
+    if (need < 0 || need > dsaidx::kTopkScratchBytes) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return DSAIDX_OK;
+    void* ws = nullptr;
+    if (need > 0) {
+        int device = -1;
+        if (hipGetDevice(&device) != hipSuccess) return DSAIDX_ERR_UNSUPPORTED;
+        if (stream) {
+            int sdev = -1;
+            if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+                return DSAIDX_ERR_HIP;
+            if (sdev != device) return DSAIDX_ERR_INVALID_ARGUMENT;
+        }
+        const hipError_t e = dsaidx::topk_scratch(device, &ws);
+        if (e != hipSuccess) return to_status(e);
+    }
+    return dsaidx_topk_per_row(logits, row_stride, lengths, rows, cols, k, out_idx, ws, need,
+                               stream);
 }
 
 // Division by the page size as a multiply and shift, exact for every

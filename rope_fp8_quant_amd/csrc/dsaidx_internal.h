@@ -82,6 +82,14 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
                        int64_t rows, int64_t cols, int32_t k, int32_t* out, void* workspace,
                        hipStream_t stream);
 
+// Workspace of the allocation-free top-k entry point: a device array of this
+// many bytes in the library's code object, one per GPU (devices 0 ..
+// kTopkScratchDevices - 1).  topk_scratch returns its address on `device`,
+// which must be the current device on the first call there.
+constexpr int64_t kTopkScratchBytes = int64_t(16) << 20;
+constexpr int kTopkScratchDevices = 64;
+hipError_t topk_scratch(int device, void** ptr);
+
 // Enqueue the stand-alone E4M3FN conversion of in[i] / scale (self-test of
 // the device encoder; scale a power of two).
 hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, float scale,

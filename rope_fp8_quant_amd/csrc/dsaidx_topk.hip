@@ -37,6 +37,8 @@
 // workspace), which spreads one row over many workgroups.
 #include "dsaidx_internal.h"
 
+#include <atomic>
+
 namespace dsaidx {
 namespace {
 
@@ -982,6 +984,31 @@ hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* l
         e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_finish_kernel),
                             dim3((unsigned)rows), dim3(kFinishT), args, 0, stream);
     return e;
+}
+
+// ------------------------------------------- allocation-free workspace ----
+// The workspace of dsaidx_topk_per_row_noalloc: a file-scope device array,
+// part of this code object, so each GPU the library runs on holds its own
+// copy until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, called once per device with that
+// device current, and is kept in a per-device table.
+static __device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+hipError_t topk_scratch(int device, void** ptr) {
+    static std::atomic<void*> table[kTopkScratchDevices];
+    if (device < 0 || device >= kTopkScratchDevices) return hipErrorInvalidDevice;
+    void* p = table[device].load(std::memory_order_acquire);
+    if (!p) {
+        // the caller made `device` current; concurrent first calls on one
+        // device look up the same address
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        table[device].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace dsaidx

@@ -102,6 +102,13 @@ hipError_t launch_hbm_stream(int mode, const void*, void*, int64_t vectors, uint
     return g_fail;
 }
 
+int g_scratch_lookups = 0;
+hipError_t topk_scratch(int, void** ptr) {
+    ++g_scratch_lookups;
+    *ptr = reinterpret_cast<void*>(uintptr_t(1) << 40);
+    return hipSuccess;
+}
+
 // The size include/dsaidx.h documents.
 int64_t topk_workspace_bytes(int64_t rows, int64_t cols, int32_t) {
     if (cols <= 32768) return 0;
@@ -119,6 +126,16 @@ hipError_t hipGetDeviceCount(int* count) {
     return hipErrorNoDevice;
 }
 hipError_t hipGetDeviceProperties(hipDeviceProp_t*, int) { return hipErrorNoDevice; }
+int g_current_device = 0;
+int g_stream_device = 0;
+hipError_t hipGetDevice(int* device) {
+    *device = g_current_device;
+    return hipSuccess;
+}
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* device) {
+    *device = g_stream_device;
+    return hipSuccess;
+}
 }
 
 namespace {
@@ -464,6 +481,33 @@ void topk_and_selftest() {
     REJECT(dsaidx_fp8_encode_selftest(nullptr, at<uint8_t>(32768), 8, 0, nullptr));
     REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 8, -127, nullptr));
     REJECT(dsaidx_fp8_encode_selftest(lg, at<uint8_t>(32768), 8, 128, nullptr));
+    // allocation-free top-k: rows of up to 32768 logits need no workspace and
+    // take the ordinary launch; a workspace beyond the library's array is
+    // refused before anything is looked up or enqueued
+    g_launches.clear();
+    CHECK(dsaidx_topk_per_row_noalloc(lg, 1000, nullptr, 3, 1000, 10, out, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].kind == 1 && g_launches[0].workspace == nullptr);
+    CHECK(dsaidx::g_scratch_lookups == 0);
+    g_launches.clear();
+    CHECK(dsaidx_topk_per_row_noalloc(lg, 1000, nullptr, 0, 131072, 10, out, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.empty());
+    REJECT(dsaidx_topk_per_row_noalloc(lg, 131072, nullptr, 228, 131072, 2048, out, nullptr));
+    REJECT(dsaidx_topk_per_row_noalloc(lg, 1000, nullptr, 3, 1000, 0, out, nullptr));
+    CHECK(dsaidx::g_scratch_lookups == 0);
+    // split rows: the library's array serves as the workspace
+    g_launches.clear();
+    CHECK(dsaidx_topk_per_row_noalloc(lg, 131072, nullptr, 227, 131072, 2048, out, nullptr) ==
+          DSAIDX_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].workspace == reinterpret_cast<void*>(uintptr_t(1) << 40));
+    CHECK(dsaidx::g_scratch_lookups == 1);
+    // a stream of another device than the current one is refused
+    g_stream_device = 1;
+    g_launches.clear();
+    CHECK(dsaidx_topk_per_row_noalloc(lg, 131072, nullptr, 4, 131072, 2048, out,
+                                      reinterpret_cast<dsaidx_stream_t>(uintptr_t(64))) ==
+          DSAIDX_ERR_INVALID_ARGUMENT);
+    CHECK(g_launches.empty());
+    g_stream_device = 0;
     // reference HBM streams: byte count in 16-byte vectors, nothing for 0 bytes
     g_launches.clear();
     CHECK(dsaidx_hbm_stream(DSAIDX_HBM_COPY, lg, at<uint8_t>(32768), 0, 0, nullptr) == DSAIDX_OK);
