@@ -14,7 +14,8 @@ of the kernel (algorithmic bytes / measured launch time against 8 TB/s), the
 oracle's CPU throughput on a bounded sample, and secondary measurements
 (decode-batch microseconds per call, the 8192-token prefill chunk with buffer
 rotation, the k-only decode path, the top-k per row and index-logits steps
-that follow, a plain-copy bandwidth reference).
+that follow, and reference HBM streams -- copy, read-only, write-only -- that
+give the achievable rate for this kernel's mix of reads and writes).
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ METRIC = "fused indexer Q/K prep tokens/s and achieved HBM GB/s (% peak); \u00b5
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (no sparsity)
 WARM_MS = 100.0      # warm-up of the bandwidth-bound secondary measurements (GPU clock ramp)
+WARM_MS_MAIN = 200.0   # warm-up of the headline measurement, on top of --warmup steps
 WARM_MS_LATENCY = 20.0   # the latency-bound decode ones (insensitive to it; keeps traces small)
 KERNEL_SOURCES = [os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", f)
                   for f in ("dsaidx_kernels.hip", "dsaidx_internal.h", "dsaidx_api.cpp")]
@@ -160,62 +162,81 @@ def time_graph(torch, fn, calls, replays, warm_ms=WARM_MS_LATENCY):
     return start.elapsed_time(end) / (calls * replays)
 
 
-def cpu_baseline(wl, target_s=5.0, min_wall_s=1.2):
-    """The oracle (as it stands) on the workload, all allowed host cores (at
-    most 16): a leading slice sized to roughly target_s of wall time, repeated
-    until at least min_wall_s has passed (with 16 threads, about 10-30 s of
-    CPU work in all)."""
+def cpu_baseline(wl, runs=3, decode_runs=100):
+    """The oracle (as it stands) on the host: the whole workload (Q and K
+    sides) on every core in this process's affinity set, median of `runs`
+    runs; the same on one thread over a leading slice; and the 64-token decode
+    batch, median of `decode_runs` calls on one thread and on all cores."""
     import numpy as np
 
     import oracle
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores = len(os.sched_getaffinity(0))
     kc = np.zeros((wl.num_slots, 128), np.uint8)
     ks = np.zeros(wl.num_slots, np.float32)
 
-    def run(n):
+    def run(n, nt):
         t0 = time.perf_counter()
         oracle.q_side(wl.q[:n], wl.weights[:n], wl.positions[:n], wl.cos, wl.sin, wl.rope_dim,
-                      wl.style, wl.weight_scale, nthreads=cores)
+                      wl.style, wl.weight_scale, nthreads=nt)
         oracle.k_side(wl.k[:n], wl.gamma, wl.beta, wl.eps, wl.positions[:n],
                       wl.out_cache_loc[:n], wl.cos, wl.sin, kc, ks, wl.rope_dim, wl.style,
-                      nthreads=cores)
+                      nthreads=nt)
         return time.perf_counter() - t0
 
-    n0 = min(wl.T, 512)
-    dt = run(n0)
-    n = int(min(wl.T, max(n0, n0 * target_s / max(dt, 1e-6))))
-    passes, total = 0, 0.0
-    while passes == 0 or total < min_wall_s:
-        total += run(n)
-        passes += 1
-    out = dict(value=passes * n / total, unit="tokens/s", cores=cores, kind="oracle",
-               sample="first %d of %d tokens of %s (Q and K sides), %d pass(es), %.2f s wall on %d "
-                      "threads" % (n, wl.T, wl.name, passes, total, cores))
-    # the same oracle on one thread, over a shorter leading slice
+    ts = sorted(run(wl.T, cores) for _ in range(runs))
+    med = ts[len(ts) // 2]
+    out = dict(value=wl.T / med, unit="tokens/s", cores=cores, kind="oracle",
+               sample="all %d tokens of %s (Q and K sides), median of %d runs (%.2f s each) on %d "
+                      "threads (every core in the affinity set)" % (wl.T, wl.name, runs, med, cores))
     n1 = min(wl.T, 2048)
-    t0 = time.perf_counter()
-    oracle.q_side(wl.q[:n1], wl.weights[:n1], wl.positions[:n1], wl.cos, wl.sin, wl.rope_dim,
-                  wl.style, wl.weight_scale, nthreads=1)
-    oracle.k_side(wl.k[:n1], wl.gamma, wl.beta, wl.eps, wl.positions[:n1], wl.out_cache_loc[:n1],
-                  wl.cos, wl.sin, kc, ks, wl.rope_dim, wl.style, nthreads=1)
-    out["single_thread"] = {"value": n1 / (time.perf_counter() - t0), "unit": "tokens/s",
-                            "sample": "first %d tokens, 1 thread" % n1}
-    # the 64-token decode batch: median microseconds per call of 100
+    t1 = sorted(run(n1, 1) for _ in range(runs))
+    out["single_thread"] = {"value": n1 / t1[len(t1) // 2], "unit": "tokens/s",
+                            "sample": "first %d tokens, 1 thread, median of %d runs" % (n1, runs)}
+    # the 64-token decode batch: median microseconds per call
     from rope_fp8_quant_amd import workloads as W
     d = W.named(1)
     dkc = np.zeros((d.num_slots, 128), np.uint8)
     dks = np.zeros(d.num_slots, np.float32)
     for label, nt in (("us_per_call_1_thread", 1), ("us_per_call_all_threads", cores)):
-        ts = []
-        for _ in range(100):
+        tt = []
+        for _ in range(decode_runs):
             t0 = time.perf_counter()
             oracle.q_side(d.q, d.weights, d.positions, d.cos, d.sin, d.rope_dim, d.style,
                           d.weight_scale, nthreads=nt)
             oracle.k_side(d.k, d.gamma, d.beta, d.eps, d.positions, d.out_cache_loc, d.cos, d.sin,
                           dkc, dks, d.rope_dim, d.style, nthreads=nt)
-            ts.append(time.perf_counter() - t0)
-        out.setdefault("decode_batch_T64", {})[label] = sorted(ts)[50] * 1e6
+            tt.append(time.perf_counter() - t0)
+        out.setdefault("decode_batch_T64", {"runs": decode_runs})[label] = sorted(tt)[decode_runs // 2] * 1e6
     return out
+
+
+def hbm_reference(torch, R, read_bytes, write_bytes, steps=20):
+    """The library's reference HBM streams (the prep kernel's access pattern:
+    16-byte nontemporal accesses, one-shot grid) over the prep call's own read
+    and write byte counts: a copy, a read-only and a write-only stream.  The
+    ideal time of a read_bytes + write_bytes mix is read_bytes / read rate +
+    write_bytes / write rate."""
+    big = max(read_bytes, write_bytes)
+    big += (-big) % 16
+    src = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(big, dtype=torch.uint8, device="cuda")
+    rb, wb = read_bytes - read_bytes % 16, write_bytes - write_bytes % 16
+    cb = (read_bytes + write_bytes) // 2
+    cb -= cb % 16
+    ms_copy = time_calls(torch, lambda: R.dsaidx_hbm_stream(R.binding.DSAIDX_HBM_COPY, src, dst, cb),
+                         steps, 3, WARM_MS)
+    ms_read = time_calls(torch, lambda: R.dsaidx_hbm_stream(R.binding.DSAIDX_HBM_READ, src, dst, rb,
+                                                            0xFFFFFFFF), steps, 3, WARM_MS)
+    ms_write = time_calls(torch, lambda: R.dsaidx_hbm_stream(R.binding.DSAIDX_HBM_WRITE, None, dst, wb,
+                                                             0x5A5A5A5A), steps, 3, WARM_MS)
+    del src, dst
+    torch.cuda.empty_cache()
+    read_gbps = rb / (ms_read * 1e-3) / 1e9
+    write_gbps = wb / (ms_write * 1e-3) / 1e9
+    return {"copy_GBps": 2 * cb / (ms_copy * 1e-3) / 1e9, "copy_bytes_moved": 2 * cb,
+            "read_only_GBps": read_gbps, "read_bytes": rb,
+            "write_only_GBps": write_gbps, "write_bytes": wb,
+            "mix_ideal_us": (read_bytes / read_gbps + write_bytes / write_gbps) / 1e3}
 
 
 def topk_measurements(torch, R, W, steps=50):
@@ -312,6 +333,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS_MAIN,
+                    help="milliseconds of warm-up calls before the timed steps (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode, prefill-chunk and k-only measurements")
@@ -351,9 +374,10 @@ def main():
     def fused():
         R.dsaidx_qk_fused(c.qa, c.ka, c.rope)
 
-    log("timing %d fused steps after %d warmup" % (args.steps, args.warmup))
+    log("timing %d fused steps after %d warmup steps and %.0f ms of warm-up calls"
+        % (args.steps, args.warmup, args.warm_ms))
     torch.cuda.synchronize()
-    ms = time_calls(torch, fused, args.steps, args.warmup)
+    ms = time_calls(torch, fused, args.steps, args.warmup, args.warm_ms)
     achieved = bytes_call / (ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(src_hash)
@@ -463,8 +487,12 @@ def main():
         extras["decode_step_T64_ctx16384"] = decode_step_measurement(torch, R, W)
         result["secondary"] = extras
 
-    # plain device copy of the same byte count: the reference for achievable
-    # bandwidth, and the calibration kernel of the HBM traffic counters
+    # what plain streams reach with this kernel's access pattern and its own
+    # read / write byte counts, and torch's device copy of the same byte count
+    rd, wr = W.bytes_per_call_split(wl.T, wl.H, "fused", wl.rope_dim)
+    ref = hbm_reference(torch, R, rd, wr)
+    ref["prep_read_bytes"], ref["prep_write_bytes"] = rd, wr
+    ref["prep_frac_of_mix_ideal"] = ref["mix_ideal_us"] / (ms * 1e3)
     n = bytes_call // 2
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -472,7 +500,9 @@ def main():
     copy_gbps = 2 * n / (msc * 1e-3) / 1e9
     result.setdefault("secondary", {})["plain_copy"] = {"bytes_moved": 2 * n,
                                                          "achieved_GBps": copy_gbps}
+    result["secondary"]["hbm_reference_streams"] = ref
     result["roofline"]["frac_of_plain_copy"] = achieved / copy_gbps
+    result["roofline"]["frac_of_mix_ideal"] = ref["prep_frac_of_mix_ideal"]
     del src, dst
 
     if not args.no_cpu_baseline:

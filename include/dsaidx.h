@@ -95,11 +95,14 @@ typedef enum dsaidx_rope_style {
  * table starts at cos + p * row_stride; likewise sin.  A single combined
  * cos_sin cache of [P, rope_dim] floats is passed as cos = cache,
  * sin = cache + rope_dim/2, row_stride = rope_dim.
- *   cos, sin      fp32, 16-byte aligned
- *   row_stride    floats between rows; >= rope_dim/2 and a multiple of 4
+ *   cos, sin      fp32, 4-byte aligned
+ *   row_stride    floats between rows; >= rope_dim/2
  *   max_position  number of table rows P >= 1
- *   rope_dim      rotated leading dims; a multiple of 16 in [16, 128]
- *   style         dsaidx_rope_style */
+ *   rope_dim      rotated leading dims; even, in [2, 128]
+ *   style         dsaidx_rope_style
+ * The kernels' vectorised rope paths serve rope_dim a multiple of 16 with
+ * 16-byte aligned tables and a row_stride that is a multiple of 4; every
+ * other valid table takes an element-wise path with the same results. */
 typedef struct dsaidx_rope {
     const float* cos;
     const float* sin;

@@ -42,14 +42,21 @@ bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>
 
 dsaidx_status check_rope(const dsaidx_rope* r) {
     if (!r->cos || !r->sin) return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (!aligned(r->cos, 16) || !aligned(r->sin, 16)) return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (r->rope_dim < 16 || r->rope_dim > dsaidx::kRow || r->rope_dim % 16 != 0)
+    if (!aligned(r->cos, 4) || !aligned(r->sin, 4)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (r->rope_dim < 2 || r->rope_dim > dsaidx::kRow || r->rope_dim % 2 != 0)
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (r->style != DSAIDX_ROPE_NEOX && r->style != DSAIDX_ROPE_INTERLEAVED)
         return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (r->row_stride < r->rope_dim / 2 || r->row_stride % 4 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (r->row_stride < r->rope_dim / 2) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (r->max_position < 1) return DSAIDX_ERR_INVALID_ARGUMENT;
     return DSAIDX_OK;
+}
+
+// The vectorised rope paths need rope_dim a multiple of 16 and 16-byte aligned
+// table rows; anything else takes the element-wise path.
+bool rope_generic(const dsaidx_rope& r) {
+    return !(r.rope_dim % 16 == 0 && r.row_stride % 4 == 0 && aligned(r.cos, 16) &&
+             aligned(r.sin, 16));
 }
 
 dsaidx_status check_q(const dsaidx_q_args* q) {
@@ -100,6 +107,7 @@ void fill_rope(PrepParams& p, const dsaidx_rope& r) {
     p.rs = r.row_stride;
     p.P = r.max_position;
     p.R = r.rope_dim;
+    p.generic = rope_generic(r) ? 1 : 0;
 }
 
 void fill_q(PrepParams& p, const dsaidx_q_args& q) {
@@ -114,10 +122,12 @@ void fill_q(PrepParams& p, const dsaidx_q_args& q) {
     p.q_scale = q.q_scale_out;
     p.weight_scale = q.weight_scale;
     p.H = q.num_heads;
+    // (the element-wise rope path has no two-token items)
     p.heads_per_item = q.num_tokens * q.num_heads <= dsaidx::kSmallBatchHeadRows
                            ? dsaidx::kHeadsPerItemSmall
-                           : (q.num_heads == dsaidx::kHeadsPerItemMid ? dsaidx::kHeadsPerItemMid
-                                                                     : dsaidx::kHeadsPerItem);
+                           : (q.num_heads == dsaidx::kHeadsPerItemMid && !p.generic
+                                  ? dsaidx::kHeadsPerItemMid
+                                  : dsaidx::kHeadsPerItem);
     if (p.heads_per_item == dsaidx::kHeadsPerItemMid) {
         // items of two tokens x 8 heads
         p.head_blocks = 1;

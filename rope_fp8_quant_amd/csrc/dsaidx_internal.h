@@ -60,6 +60,7 @@ struct PrepParams {
     int64_t T;
     float eps;
     // rope table
+    int32_t generic;       // host only: element-wise rope path (see the kernel)
     int32_t R;
     const float* cos;
     const float* sin;

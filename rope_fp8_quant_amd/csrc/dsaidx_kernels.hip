@@ -18,6 +18,11 @@
 //          lanes j and j + R/8.  Used for NeoX with rope_dim <= 64 and for the
 //          interleaved style (pairs never leave a lane).
 //   contig lane j holds [8j, 8j+8); used for NeoX with rope_dim 80..128.
+//   generic the contig placement with an element-wise rotation, for every other
+//          rope_dim (any even value up to 128) and for tables whose rows are
+//          not 16-byte aligned: each lane reads the cos/sin entries of its own
+//          rope elements, and the partner values come through a small LDS row
+//          buffer per wavefront.  Not tuned: the workloads use the two above.
 // Row reductions (max |y|, LayerNorm sums) are four DPP row_ror steps; the
 // NeoX partner values come from ds_bpermute.  A query work item is one token
 // and HPI heads (HPI / 4 passes of 4 vectors): the token's cos/sin sit in
@@ -64,6 +69,7 @@ namespace {
 
 constexpr int kContig = 0;
 constexpr int kSplit = 1;
+constexpr int kGeneric = 2;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -119,7 +125,7 @@ __device__ __forceinline__ void store4(uint8_t* p, uint32_t c) {
 // The lane's eight bf16 values of one 128-element row (layout order).
 template <int LAYOUT>
 __device__ __forceinline__ uint4 load_row(const uint16_t* row, int j) {
-    if (LAYOUT == kContig) return load16(row + 8 * j);
+    if (LAYOUT != kSplit) return load16(row + 8 * j);
     const uint2 a = load8(row + 4 * j);
     const uint2 b = load8(row + 64 + 4 * j);
     return make_uint4(a.x, a.y, b.x, b.y);
@@ -128,7 +134,7 @@ __device__ __forceinline__ uint4 load_row(const uint16_t* row, int j) {
 // The lane's eight codes of one 128-byte code row.
 template <int LAYOUT>
 __device__ __forceinline__ void store_row(uint8_t* row, int j, uint2 c) {
-    if (LAYOUT == kContig) {
+    if (LAYOUT != kSplit) {
         store8(row + 8 * j, c);
     } else {
         store4(row + 4 * j, c.x);
@@ -140,8 +146,8 @@ __device__ __forceinline__ void store_row(uint8_t* row, int j, uint2 c) {
 template <int LAYOUT>
 __device__ __forceinline__ void load_params(const float* v, int j, float out[8]) {
     const float4* p = reinterpret_cast<const float4*>(v);
-    const float4 a = LAYOUT == kContig ? p[2 * j] : p[j];
-    const float4 b = LAYOUT == kContig ? p[2 * j + 1] : p[16 + j];
+    const float4 a = LAYOUT != kSplit ? p[2 * j] : p[j];
+    const float4 b = LAYOUT != kSplit ? p[2 * j + 1] : p[16 + j];
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
@@ -245,13 +251,18 @@ __device__ __forceinline__ uint2 encode8(const float y[8], float scale) {
 //   split interleaved: the first four values hold pairs 2j, 2j+1 (c[0..1],
 //     s[0..1]) when 4j < R, the last four pairs 32+2j, 33+2j (c[2..3],
 //     s[2..3]) when 64 + 4j < R.
-// For NeoX the sine carries the pair's sign: a*c - b*s == a*c + b*(-s) exactly.
+//   generic: c[m], s[m] for the lane's element m = 8j + m when it is below R
+//     (bit m of mask), for either style.
+// For NeoX the sine carries the pair's sign: a*c - b*s == a*c + b*(-s) exactly
+// (in the generic layout for both styles).
 struct RopeLane {
     float c[8];
     float s[8];
     int partner_addr;  // ds_bpermute byte address of the NeoX partner lane
     bool active;       // NeoX: the lane rotates; interleaved: first four values rotate
     bool active_hi;    // interleaved: last four values rotate
+    uint32_t mask;     // generic: the lane's elements that rotate
+    int rdim;          // generic: rope_dim
 };
 
 template <int STYLE, int LAYOUT>
@@ -263,6 +274,27 @@ __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, 
     const float* srow = p.sin + pos * p.rs;
     r.active_hi = false;
     r.partner_addr = lane << 2;
+    r.mask = 0;
+    r.rdim = R;
+    if constexpr (LAYOUT == kGeneric) {
+        // element e = 8j + m rotates with pair i: NeoX i = e mod R/2 (the
+        // first half carries -sin), interleaved i = e / 2 (even e carries -sin)
+        const int half = R >> 1;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int e = 8 * j + m;
+            r.c[m] = 0.0f;
+            r.s[m] = 0.0f;
+            if (e < R) {
+                const bool first = STYLE == 0 ? e < half : (e & 1) == 0;
+                const int i = STYLE == 0 ? (first ? e : e - half) : (e >> 1);
+                r.c[m] = crow[i];
+                r.s[m] = first ? -srow[i] : srow[i];
+                r.mask |= 1u << m;
+            }
+        }
+        return r;
+    }
     if (STYLE == 0) {
         // lanes per half of the rope slice
         const int hl = LAYOUT == kContig ? (R >> 4) : (R >> 3);
@@ -332,9 +364,47 @@ __device__ __forceinline__ void rotate_neox(float x[8], const float xp[8], const
     }
 }
 
+// Element-wise RoPE of the generic layout.  Each DPP row of the wavefront
+// writes its vector to its own 128-float slot of an LDS buffer and reads the
+// partners back by index (NeoX: e +- R/2; interleaved: e ^ 1).  Only the
+// wavefront's own slots are touched, and a wavefront's LDS accesses complete
+// in issue order, so no workgroup barrier is involved: the wave barriers only
+// keep the compiler from moving the accesses across each other.
+template <int STYLE>
+__device__ __forceinline__ void rope_generic(float x[8], const RopeLane& rl) {
+    __shared__ __align__(16) float xchg[256 / 64][kRowsPerWave][kRow];
+    const int lane = threadIdx.x & 63;
+    const int j = lane & (kLanesPerRow - 1);
+    float* row = xchg[threadIdx.x >> 6][lane >> 4];
+    *reinterpret_cast<float4*>(row + 8 * j) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(row + 8 * j + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    __builtin_amdgcn_wave_barrier();
+    const int half = rl.rdim >> 1;
+    float xp[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int e = 8 * j + m;
+        const int partner = STYLE == 0 ? (e < half ? e + half : e - half) : (e ^ 1);
+        xp[m] = (rl.mask >> m) & 1u ? row[partner] : 0.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        if ((rl.mask >> m) & 1u) {
+            const float xc = x[m] * rl.c[m];
+            const float ps = xp[m] * rl.s[m];
+            x[m] = xc + ps;
+        }
+    }
+}
+
 // RoPE of one row held as eight fp32 values per lane.
 template <int STYLE, int LAYOUT>
 __device__ __forceinline__ void rope_row(float x[8], const RopeLane& rl) {
+    if constexpr (LAYOUT == kGeneric) {
+        rope_generic<STYLE>(x, rl);
+        return;
+    }
     if (STYLE == 0) {
         float xp[8];
         if (LAYOUT == kContig) {
@@ -365,6 +435,10 @@ __device__ __forceinline__ void rope_row(float x[8], const RopeLane& rl) {
 template <int STYLE, int LAYOUT>
 __device__ __forceinline__ void rope_packed_row(const uint4& raw, float x[8], const RopeLane& rl) {
     unpack8(raw, x);
+    if constexpr (LAYOUT == kGeneric) {
+        rope_generic<STYLE>(x, rl);
+        return;
+    }
     if (STYLE == 0) {
         uint4 pr = raw;
         pr.x = (uint32_t)__builtin_amdgcn_ds_bpermute(rl.partner_addr, (int)raw.x);
@@ -678,7 +752,18 @@ hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned b
                                          : reinterpret_cast<const void*>(k16);
     };
     const void* fn;
-    if (style == 1)
+    if (p.generic)
+        fn = style == 1 ? (hpi == kHeadsPerItemSmall
+                               ? reinterpret_cast<const void*>(
+                                     &indexer_qk_prep_kernel<1, kGeneric, kHeadsPerItemSmall, false>)
+                               : reinterpret_cast<const void*>(
+                                     &indexer_qk_prep_kernel<1, kGeneric, kHeadsPerItem, false>))
+                        : (hpi == kHeadsPerItemSmall
+                               ? reinterpret_cast<const void*>(
+                                     &indexer_qk_prep_kernel<0, kGeneric, kHeadsPerItemSmall, false>)
+                               : reinterpret_cast<const void*>(
+                                     &indexer_qk_prep_kernel<0, kGeneric, kHeadsPerItem, false>));
+    else if (style == 1)
         fn = pick(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, true>,
                   &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, false>,
                   &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid, false>,

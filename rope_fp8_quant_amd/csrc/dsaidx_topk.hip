@@ -944,45 +944,75 @@ static hipError_t launch_row(RowArgs& a, int64_t rows, hipStream_t stream) {
                            dim3((unsigned)rows), dim3(T), args, 0, stream);
 }
 
+// A dispatch counts its work-items in 32 bits: rows are launched in batches
+// whose workgroups * threads stay below 2^32 (one batch, so one or four
+// dispatches, for any call of up to 4194303 rows; more only beyond that).
+constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;
+
+static hipError_t launch_rows(const RowArgs& base, int variant, int64_t rows, hipStream_t stream) {
+    constexpr int kThreads[4] = {512, 512, 1024, 1024};   // DSAIDX_TOPK_R4K .. R32K
+    const int64_t batch = kMaxItems / kThreads[variant];
+    hipError_t e = hipSuccess;
+    for (int64_t r0 = 0; r0 < rows && e == hipSuccess; r0 += batch) {
+        const int64_t n = rows - r0 < batch ? rows - r0 : batch;
+        RowArgs a = base;
+        a.logits = base.logits + r0 * base.row_stride;
+        a.lengths = base.lengths ? base.lengths + r0 : nullptr;
+        a.out = base.out + r0 * base.k;
+        switch (variant) {
+            case 0: e = launch_row<DSAIDX_TOPK_R4K>(a, n, stream); break;
+            case 1: e = launch_row<DSAIDX_TOPK_R8K>(a, n, stream); break;
+            case 2: e = launch_row<DSAIDX_TOPK_R16K>(a, n, stream); break;
+            default: e = launch_row<DSAIDX_TOPK_R32K>(a, n, stream); break;
+        }
+    }
+    return e;
+}
+
 hipError_t launch_topk(const float* logits, int64_t row_stride, const int32_t* lengths,
                        int64_t rows, int64_t cols, int32_t k, int32_t* out, void* workspace,
                        hipStream_t stream) {
     const TopkPlan p = plan_topk(rows, cols, k);
     if (!p.split) {
         RowArgs a{logits, row_stride, lengths, cols, k, out, rows >= kManyRows ? 1 : 0};
-        switch (p.variant) {
-            case 0: return launch_row<DSAIDX_TOPK_R4K>(a, rows, stream);
-            case 1: return launch_row<DSAIDX_TOPK_R8K>(a, rows, stream);
-            case 2: return launch_row<DSAIDX_TOPK_R16K>(a, rows, stream);
-            default: return launch_row<DSAIDX_TOPK_R32K>(a, rows, stream);
-        }
+        return launch_rows(a, p.variant, rows, stream);
     }
-    SplitArgs sa{};
-    sa.logits = logits;
-    sa.row_stride = row_stride;
-    sa.lengths = lengths;
-    sa.cols = cols;
-    sa.k = k;
-    sa.chunks = (int32_t)p.chunks;
-    sa.out = out;
     const int64_t cap = split_list_cap(cols);
-    sa.state = static_cast<uint32_t*>(workspace);
-    sa.list_key = sa.state + rows * kStateWords;
-    sa.list_pos = reinterpret_cast<int32_t*>(sa.list_key + rows * cap);
-    sa.list_stride = cap;
-    void* args[] = {&sa};
-    const dim3 grid((unsigned)(rows * p.chunks));
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_zero_kernel),
-                                   dim3((unsigned)rows), dim3(kSplitT), args, 0, stream);
-    if (e == hipSuccess)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_hist_kernel), grid,
-                            dim3(kSplitT), args, 0, stream);
-    if (e == hipSuccess)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_select_kernel), grid,
-                            dim3(kSplitT), args, 0, stream);
-    if (e == hipSuccess)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_finish_kernel),
-                            dim3((unsigned)rows), dim3(kFinishT), args, 0, stream);
+    uint32_t* state = static_cast<uint32_t*>(workspace);
+    uint32_t* list_key = state + rows * kStateWords;
+    int32_t* list_pos = reinterpret_cast<int32_t*>(list_key + rows * cap);
+    // rows * chunks workgroups of kSplitT threads, rows of kFinishT
+    int64_t batch = kMaxItems / (kSplitT * p.chunks);
+    if (batch > kMaxItems / kFinishT) batch = kMaxItems / kFinishT;
+    hipError_t e = hipSuccess;
+    for (int64_t r0 = 0; r0 < rows && e == hipSuccess; r0 += batch) {
+        const int64_t n = rows - r0 < batch ? rows - r0 : batch;
+        SplitArgs sa{};
+        sa.logits = logits + r0 * row_stride;
+        sa.row_stride = row_stride;
+        sa.lengths = lengths ? lengths + r0 : nullptr;
+        sa.cols = cols;
+        sa.k = k;
+        sa.chunks = (int32_t)p.chunks;
+        sa.out = out + r0 * k;
+        sa.state = state + r0 * kStateWords;
+        sa.list_key = list_key + r0 * cap;
+        sa.list_pos = list_pos + r0 * cap;
+        sa.list_stride = cap;
+        void* args[] = {&sa};
+        const dim3 grid((unsigned)(n * p.chunks));
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_zero_kernel),
+                            dim3((unsigned)n), dim3(kSplitT), args, 0, stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_hist_kernel), grid,
+                                dim3(kSplitT), args, 0, stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_select_kernel), grid,
+                                dim3(kSplitT), args, 0, stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_split_finish_kernel),
+                                dim3((unsigned)n), dim3(kFinishT), args, 0, stream);
+    }
     return e;
 }
 

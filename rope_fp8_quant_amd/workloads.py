@@ -215,6 +215,17 @@ def bytes_per_token(H: int = 64, entry: str = "fused", rope_dim: int = 64,
     return q_side + k_side - 8   # fused: the position is read once per token
 
 
+def bytes_per_call_split(T: int, H: int = 64, entry: str = "fused", rope_dim: int = 64):
+    """(read, written) algorithmic bytes of one call; they sum to
+    bytes_per_call.  Reads: q, weights, position, cos/sin, k, slot, gamma and
+    beta; writes: q_fp8, weights_out, the key's code row and scale."""
+    writes_q = H * ROW + H * 4
+    writes_k = ROW + 4
+    writes = (0 if entry == "k" else writes_q) + (0 if entry == "q" else writes_k)
+    total = bytes_per_call(T, H, entry, rope_dim)
+    return total - T * writes, T * writes
+
+
 def bytes_per_call(T: int, H: int = 64, entry: str = "fused", rope_dim: int = 64) -> int:
     """bytes_per_token * T, plus the LayerNorm gamma and beta (fp32 [128] each)
     once per call for the entries that run K rows."""

@@ -236,6 +236,11 @@ def check_k(out: dict, wl: W.Workload, report: dict, cache_row_pad=0, k_flags=0,
     assert np.all(got_kc[~touched] == SENTINEL), "cache rows outside out_cache_loc changed"
     assert np.all(got_kc[:, ROW:] == SENTINEL), "cache row padding changed"
     compare_codes(got_kc[touched, :ROW], kc[touched, :ROW], "k_cache", report)
+    # Beyond the acceptance rule: on these seeded inputs the kernels' fp64
+    # LayerNorm sums (a different order from the oracle's) leave the fp32 mean,
+    # variance and reciprocal root the same, so the codes match byte for byte.
+    # The kernels are deterministic, so this holds run after run.
+    assert report["k_cache"]["bytes_differ"] == 0, report["k_cache"]
 
 
 # ------------------------------------------------------- index logits ----

@@ -352,14 +352,38 @@ void rejected_arguments() {
         REJECT(dsaidx_k_norm_rope_quant_store(&k, &r, nullptr));
         REJECT(dsaidx_qk_fused(&q, &k, &r, nullptr));
     };
+    // rope_dim not a multiple of 16, a row stride not a multiple of 4 or rows
+    // not 16-byte aligned: the element-wise path, never two-token items
+    {
+        auto path = [&](void (*edit)(dsaidx_rope&), int64_t T, int32_t H) {
+            dsaidx_rope r = rope;
+            edit(r);
+            dsaidx_q_args q = make_q(T, H);
+            dsaidx_k_args k = make_k(T);
+            g_launches.clear();
+            CHECK(dsaidx_qk_fused(&q, &k, &r, nullptr) == DSAIDX_OK);
+            CHECK(g_launches.size() == 1);
+            return g_launches.empty() ? Launch{} : g_launches[0];
+        };
+        CHECK(path([](dsaidx_rope&) {}, 64, 64).p.generic == 0);
+        CHECK(path([](dsaidx_rope& r) { r.rope_dim = 24; }, 64, 64).p.generic == 1);
+        CHECK(path([](dsaidx_rope& r) { r.rope_dim = 2; r.row_stride = 1; }, 64, 64).p.generic == 1);
+        CHECK(path([](dsaidx_rope& r) { r.row_stride = 33; }, 64, 64).p.generic == 1);
+        CHECK(path([](dsaidx_rope& r) { r.sin = at<const float>(1028); }, 64, 64).p.generic == 1);
+        const Launch fast8 = path([](dsaidx_rope&) {}, 65536, 8);
+        CHECK(fast8.p.generic == 0 && fast8.p.heads_per_item == 8);
+        const Launch slow8 = path([](dsaidx_rope& r) { r.row_stride = 33; }, 65536, 8);
+        CHECK(slow8.p.generic == 1 && slow8.p.heads_per_item == 16 && slow8.p.q_items == 65536);
+        g_launches.clear();
+    }
     bad_rope([](dsaidx_rope& r) { r.cos = nullptr; });
-    bad_rope([](dsaidx_rope& r) { r.sin = at<const float>(1028); });      // not 16-byte aligned
+    bad_rope([](dsaidx_rope& r) { r.sin = at<const float>(1026); });      // not 4-byte aligned
     bad_rope([](dsaidx_rope& r) { r.rope_dim = 0; });
-    bad_rope([](dsaidx_rope& r) { r.rope_dim = 24; });                    // not a multiple of 16
+    bad_rope([](dsaidx_rope& r) { r.rope_dim = 23; });                    // odd
     bad_rope([](dsaidx_rope& r) { r.rope_dim = 144; });
     bad_rope([](dsaidx_rope& r) { r.style = 2; });
     bad_rope([](dsaidx_rope& r) { r.row_stride = 16; });                  // < rope_dim / 2
-    bad_rope([](dsaidx_rope& r) { r.row_stride = 34; });                  // not a multiple of 4
+    bad_rope([](dsaidx_rope& r) { r.rope_dim = 10; r.row_stride = 4; });  // < rope_dim / 2
     bad_rope([](dsaidx_rope& r) { r.max_position = 0; });
     // query side
     auto bad_q = [&](void (*edit)(dsaidx_q_args&)) {

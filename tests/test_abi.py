@@ -126,9 +126,12 @@ def test_null_structs_rejected(L):
     assert L.dsaidx_qk_fused(ctypes.byref(good_q()), None, ctypes.byref(good_rope()), None) == 1
 
 
-BAD_ROPE = [dict(cos=None), dict(sin=None), dict(cos=FAKE + 4), dict(rope_dim=0),
-            dict(rope_dim=8), dict(rope_dim=48 + 8), dict(rope_dim=144), dict(style=2),
-            dict(style=-1), dict(row_stride=16), dict(row_stride=34), dict(max_position=0)]
+BAD_ROPE = [dict(cos=None), dict(sin=None), dict(cos=FAKE + 2), dict(sin=FAKE + 1),
+            dict(rope_dim=0), dict(rope_dim=-2), dict(rope_dim=7), dict(rope_dim=63),
+            dict(rope_dim=130), dict(rope_dim=144), dict(style=2), dict(style=-1),
+            dict(row_stride=16), dict(rope_dim=6, row_stride=2), dict(max_position=0)]
+GOOD_ROPE = [dict(rope_dim=2, row_stride=1), dict(rope_dim=6, row_stride=3), dict(rope_dim=126, row_stride=63),
+             dict(rope_dim=24), dict(row_stride=34), dict(cos=FAKE + 4, sin=FAKE + 8), dict(style=1, rope_dim=10)]
 
 
 @pytest.mark.parametrize("kw", BAD_ROPE, ids=lambda d: str(d))
@@ -136,6 +139,16 @@ def test_bad_rope_rejected(L, kw):
     r = good_rope(**kw)
     assert call_q(L, good_q(), r) == B.DSAIDX_ERR_INVALID_ARGUMENT
     assert call_k(L, good_k(), r) == B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", GOOD_ROPE, ids=lambda d: str(d))
+def test_every_even_rope_dim_and_table_stride_accepted(L, kw):
+    """Any even rope_dim in [2, 128] and any row stride >= rope_dim / 2 with
+    4-byte aligned tables passes the checks (the launch itself then fails on a
+    machine without a GPU, with a status other than INVALID_ARGUMENT)."""
+    r = good_rope(**kw)
+    assert call_q(L, good_q(), r) != B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_k(L, good_k(), r) != B.DSAIDX_ERR_INVALID_ARGUMENT
 
 
 BAD_Q = [dict(q=None), dict(weights=None), dict(positions=None), dict(q_fp8=None),

@@ -277,8 +277,11 @@ def test_two_token_items_on_strided_views():
 
 
 @pytest.mark.parametrize("style", [W.NEOX, W.INTERLEAVED])
-@pytest.mark.parametrize("rope_dim", [16, 32, 48, 64, 80, 96, 112, 128])
+@pytest.mark.parametrize("rope_dim", [2, 6, 8, 16, 24, 32, 40, 48, 64, 72, 80, 96, 112, 126, 128])
 def test_rope_dims(rope_dim, style):
+    """Every even rope_dim is accepted: multiples of 16 take the vectorised
+    paths (contiguous [P, rope_dim/2] tables), the others the element-wise
+    one; both styles, against the oracle."""
     wl = W.make(29, 16, rope_dim=rope_dim, style=style, table_rows=3000, num_slots=100,
                 seed=rope_dim * 2 + style)
     c = DeviceCase(wl)
@@ -287,6 +290,68 @@ def test_rope_dims(rope_dim, style):
     rep = {}
     check_q(out, wl, rep)
     check_k(out, wl, rep)
+
+
+def padded_tables(wl, pad):
+    """cos / sin as [P, rope_dim/2] views of [P, rope_dim/2 + pad] buffers (a
+    row stride the vectorised paths do not take when it is not a multiple of
+    4, or rows that are not 16-byte aligned)."""
+    half = wl.rope_dim // 2
+    P = wl.cos.shape[0]
+    bc = torch.zeros((P, half + pad), dtype=torch.float32, device="cuda")
+    bs = torch.zeros((P, half + pad), dtype=torch.float32, device="cuda")
+    bc[:, :half] = dev(wl.cos)
+    bs[:, :half] = dev(wl.sin)
+    return bc[:, :half], bs[:, :half]
+
+
+@pytest.mark.parametrize("T,H,rope_dim,style", [(29, 16, 64, W.NEOX), (29, 16, 128, W.NEOX),
+                                                (41, 64, 64, W.INTERLEAVED), (300, 64, 96, W.NEOX),
+                                                (4099, 8, 64, W.NEOX), (700, 33, 32, W.INTERLEAVED)])
+def test_element_wise_rope_equals_vectorised(T, H, rope_dim, style):
+    """Tables with an odd row stride send a multiple-of-16 rope_dim down the
+    element-wise path: the same bytes as the vectorised path on contiguous
+    tables, through every entry (4-head, 16-head and, at 8 heads, in place of
+    the two-token items)."""
+    wl = W.make(T, H, rope_dim=rope_dim, style=style, table_rows=8192, num_slots=T + 64,
+                slot_mode="perm_prefix", seed=900 + T + rope_dim + style)
+    print("\n[case] element-wise rope T=%d H=%d rope_dim=%d style=%d" % (T, H, rope_dim, style),
+          flush=True)
+    fast = DeviceCase(wl)
+    fast.run("fused")
+    slow = DeviceCase(wl)
+    slow.cos, slow.sin = padded_tables(wl, 1)
+    assert slow.cos.stride(0) % 4 != 0
+    slow.run("fused")
+    a, b = fast.host(), slow.host()
+    for key in ("q_fp8", "w_out", "q_scale", "k_cache", "k_scale"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+    slow.q_fp8.fill_(SENTINEL)
+    slow.run("q")
+    assert np.array_equal(slow.host()["q_fp8"], a["q_fp8"])
+    k1 = DeviceCase(wl)
+    k1.cos, k1.sin = padded_tables(wl, 3)
+    k1.run("k_only")
+    assert np.array_equal(k1.host()["k_cache"], a["k_cache"])
+    rep = {}
+    check_q(b, wl, rep)
+    check_k(b, wl, rep)
+
+
+@pytest.mark.parametrize("rope_dim", [6, 126])
+def test_element_wise_rope_combined_table(rope_dim):
+    """A combined [P, rope_dim] cos_sin cache with rope_dim/2 odd: sin starts
+    rope_dim/2 floats into each row (4-byte aligned only), row stride
+    rope_dim.  Large batch (16-head items) and both styles."""
+    for style in (W.NEOX, W.INTERLEAVED):
+        wl = W.make(1100, 64, rope_dim=rope_dim, style=style, table_rows=2048, num_slots=2048,
+                    seed=rope_dim + style)
+        c = DeviceCase(wl, combined_table=True)
+        c.run("fused")
+        out = c.host()
+        rep = {}
+        check_q(out, wl, rep)
+        check_k(out, wl, rep)
 
 
 def test_zero_rows_smaller_instance():
@@ -615,6 +680,7 @@ def test_offsets_beyond_2_pow_31_elements():
     got_kc = k_cache[t_dev].cpu().numpy()
     rep = {}
     compare_codes(got_kc, kc, "k_cache", rep)
+    assert rep["k_cache"]["bytes_differ"] == 0, rep
     assert np.array_equal(k_scale[t_dev].cpu().numpy(), ks)
     assert np.all(k_cache[T:].cpu().numpy() == SENTINEL)
     rep["tokens_checked"] = int(len(tokens))
@@ -636,7 +702,7 @@ def test_random_combinations(seed):
     else:
         T = int(rng.choice([1, 3, 41, 64, 130, 255, 256, 257, 700]))
         H = int(rng.choice([1, 4, 7, 16, 33, 64, 80]))
-    rope_dim = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    rope_dim = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128, 2, 10, 36, 58, 100, 126]))
     style = int(rng.choice([W.NEOX, W.INTERLEAVED]))
     values = str(rng.choice(["normal", "student_t3", "outlier_channels", "sparse_outliers",
                              "zero_rows"]))
