@@ -37,7 +37,8 @@ WARM_MS = 100.0      # warm-up of the bandwidth-bound secondary measurements (GP
 WARM_MS_MAIN = 200.0   # warm-up of the headline measurement, on top of --warmup steps
 WARM_MS_LATENCY = 20.0   # the latency-bound decode ones (insensitive to it; keeps traces small)
 KERNEL_SOURCES = [os.path.join(ROOT, "rope_fp8_quant_amd", "csrc", f)
-                  for f in ("dsaidx_kernels.hip", "dsaidx_internal.h", "dsaidx_api.cpp")]
+                  for f in ("dsaidx_kernels.hip", "dsaidx_prep_device.h", "dsaidx_internal.h",
+                            "dsaidx_api.cpp")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_indexer_qk_prep_long_prefill_T65536.txt")
 
 
@@ -297,6 +298,46 @@ def logits_measurements(torch, R, W, steps=20):
     return out
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (no sparsity)
+
+
+def proj_measurement(torch, R, W, steps=20):
+    """The key / head-gate projection with the key preparation in its
+    epilogue, at the long-prefill size: hidden [65536, 7168] bf16 times the
+    [192, 7168] weight on the matrix cores, the 128 key columns prepared into
+    the 262144-slot cache, the 64 gate columns written as bf16."""
+    T, d, H = 65536, 7168, 64
+    pw = W.proj_make(T, d, H, seed=4004, name="proj_long_prefill_T65536", table_rows=262144,
+                     pos_mode="contiguous", pos_lo=196608, num_slots=262144, slot_mode="contiguous")
+    kw = pw.key
+
+    def bf16(a):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    hid, wt = bf16(pw.hidden), bf16(pw.weight)
+    gates = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    pos = torch.from_numpy(kw.positions).cuda()
+    loc = torch.from_numpy(kw.out_cache_loc).cuda()
+    gam, bet = torch.from_numpy(kw.gamma).cuda(), torch.from_numpy(kw.beta).cuda()
+    cos, sin = torch.from_numpy(kw.cos).cuda(), torch.from_numpy(kw.sin).cuda()
+    kc = torch.zeros((kw.num_slots, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((kw.num_slots,), dtype=torch.float32, device="cuda")
+    pa = R.proj_args(hid, wt, gates)
+    ka = R.k_args(None, gam, bet, kw.eps, pos, loc, kc, ks)
+    ra = R.rope_args(cos, sin, kw.rope_dim, kw.style)
+    call = lambda: R.dsaidx_proj_k_norm_rope_quant_store(pa, ka, ra)
+    ms = time_calls(torch, call, steps, 3, WARM_MS)
+    bt = W.proj_bytes_per_call(T, d, H, kw.rope_dim)
+    fl = W.proj_flops_per_call(T, d, H)
+    del hid, wt, gates, kc, ks
+    torch.cuda.empty_cache()
+    return {"us_per_call": ms * 1e3, "T": T, "d": d, "H": H, "algorithmic_bytes": bt,
+            "achieved_GBps": bt / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": bt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "algorithmic_flops": fl, "achieved_TFLOPs": fl / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def decode_step_measurement(torch, R, W):
     """One indexer decode step for a 64-request batch at a 16384-key context,
     replayed from a HIP graph: the fused prep call (64 tokens into a
@@ -342,6 +383,8 @@ def main():
                     help="time only the top-k-per-row workloads (a JSON object of its own)")
     ap.add_argument("--logits-only", action="store_true",
                     help="time only the index-logits workloads (a JSON object of its own)")
+    ap.add_argument("--proj-only", action="store_true",
+                    help="time only the projection with the key preparation in its epilogue")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -360,6 +403,10 @@ def main():
         raise SystemExit("cuda:0 is not a gfx950 device")
     if args.topk_only:
         print(json.dumps({"topk_per_row": topk_measurements(torch, R, W, args.steps)}), flush=True)
+        return
+    if args.proj_only:
+        print(json.dumps({"proj_long_prefill_T65536_d7168": proj_measurement(torch, R, W, args.steps)}),
+              flush=True)
         return
     if args.logits_only:
         print(json.dumps({"mqa_logits": logits_measurements(torch, R, W, min(args.steps, 50))}),
@@ -485,6 +532,7 @@ def main():
         extras.update(topk_measurements(torch, R, W))
         extras.update(logits_measurements(torch, R, W))
         extras["decode_step_T64_ctx16384"] = decode_step_measurement(torch, R, W)
+        extras["proj_long_prefill_T65536_d7168"] = proj_measurement(torch, R, W)
         result["secondary"] = extras
 
     # what plain streams reach with this kernel's access pattern and its own

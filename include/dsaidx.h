@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define DSAIDX_ABI_VERSION 5
+#define DSAIDX_ABI_VERSION 6
 #define DSAIDX_HEAD_DIM 128 /* width of every head vector and K row */
 
 typedef struct ihipStream_t* dsaidx_stream_t; /* the same type as hipStream_t */
@@ -237,6 +237,50 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
 dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_rope* rope,
                                           dsaidx_stream_t stream);
 
+/* The indexer's key and head-gate projection with the key preparation in its
+ * epilogue: the fused wk_weights_proj GEMM of [sglang-fuse] Motivation, whose
+ * bf16 output the unfused path writes and the preparation reads back.
+ *   out[t, n] = bf16( sum_c hidden[t, c] * weight[n, c] )   (fp32 accumulation)
+ *   n < 128:      the key row of token t, prepared exactly as
+ *                 dsaidx_k_norm_rope_quant_store prepares a k of these bf16
+ *                 values (LayerNorm, RoPE, quantisation, cache store);
+ *   128 <= n < 128 + H:  the head gate of head n - 128, written to gates_out
+ *                 (the weights input of dsaidx_q_rope_quant_fold).
+ * The products are exact in fp32 and the sums are fp32 in an order the
+ * library chooses; the bf16 rounding is to nearest even.
+ *   hidden         bf16 [T, d]: token t at hidden + t * hidden_stride_t; 16-byte
+ *                  aligned; hidden_stride_t >= d, a multiple of 8
+ *   weight         bf16 [128 + H, d] (a Linear layer's [out, in] layout): row n
+ *                  at weight + n * weight_stride_n; 16-byte aligned;
+ *                  weight_stride_n >= d, a multiple of 8
+ *   hidden_dim     d: a multiple of 64 in [64, 2^20]
+ *   num_heads      H in [1, 64]
+ *   gates_out      out: bf16 [T, H], token stride gates_stride_t >= H; 2-byte aligned
+ *   k_out          out: bf16 [T, 128] (token stride k_out_stride_t >= 128, a
+ *                  multiple of 8; 16-byte aligned), or NULL: the projected key as
+ *                  the GEMM would write it
+ * The key side comes from `k` as for dsaidx_k_norm_rope_quant_store, except
+ * that k->k and k->k_stride_t are not used (the key comes from the
+ * projection): num_tokens, LayerNorm parameters, positions, out_cache_loc,
+ * cache and flags.  One dispatch; T == 0 launches nothing. */
+typedef struct dsaidx_proj_args {
+    const uint16_t* hidden;
+    int64_t hidden_stride_t;
+    const uint16_t* weight;
+    int64_t weight_stride_n;
+    int64_t hidden_dim;
+    int32_t num_heads;
+    int32_t reserved;   /* 0 */
+    uint16_t* gates_out;
+    int64_t gates_stride_t;
+    uint16_t* k_out;
+    int64_t k_out_stride_t;
+} dsaidx_proj_args;
+
+dsaidx_status dsaidx_proj_k_norm_rope_quant_store(const dsaidx_proj_args* proj,
+                                                  const dsaidx_k_args* k, const dsaidx_rope* rope,
+                                                  dsaidx_stream_t stream);
+
 /* Top-k per row: the selection that follows the index logits, each query
  * keeping its index_topk highest-scoring keys ([sglang-fuse] Benchmark:
  * index_topk = 2048; [vllm-47335] Kernel-level evidence: the top-k-per-row
@@ -392,8 +436,8 @@ const char* dsaidx_status_string(dsaidx_status status);
 int dsaidx_abi_version(void);
 
 /* sizeof the argument structs as built (0 = dsaidx_rope, 1 = dsaidx_q_args,
- * 2 = dsaidx_k_args, 3 = dsaidx_logits_args; anything else returns 0), for
- * binding checks. */
+ * 2 = dsaidx_k_args, 3 = dsaidx_logits_args, 4 = dsaidx_proj_args; anything
+ * else returns 0), for binding checks. */
 size_t dsaidx_struct_size(int which);
 
 #ifdef __cplusplus

@@ -29,7 +29,8 @@ EXPORTED = ("dsaidx_q_rope_quant_fold", "dsaidx_k_norm_rope_quant_store", "dsaid
             "dsaidx_k_only_prepare_store", "dsaidx_device_supported", "dsaidx_status_string",
             "dsaidx_abi_version", "dsaidx_struct_size", "dsaidx_fp8_encode_selftest",
             "dsaidx_topk_per_row", "dsaidx_topk_workspace_bytes", "dsaidx_mqa_logits",
-            "dsaidx_hbm_stream", "dsaidx_topk_per_row_noalloc")
+            "dsaidx_hbm_stream", "dsaidx_topk_per_row_noalloc",
+            "dsaidx_proj_k_norm_rope_quant_store")
 TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -75,6 +76,15 @@ class DsaidxLogitsArgs(ctypes.Structure):
                 ("logits_stride", ctypes.c_int64)]
 
 
+class DsaidxProjArgs(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_void_p), ("hidden_stride_t", ctypes.c_int64),
+                ("weight", ctypes.c_void_p), ("weight_stride_n", ctypes.c_int64),
+                ("hidden_dim", ctypes.c_int64), ("num_heads", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("gates_out", ctypes.c_void_p),
+                ("gates_stride_t", ctypes.c_int64), ("k_out", ctypes.c_void_p),
+                ("k_out_stride_t", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -96,7 +106,10 @@ def lib() -> ctypes.CDLL:
                            ("dsaidx_qk_fused", [ctypes.POINTER(DsaidxQArgs),
                                                 ctypes.POINTER(DsaidxKArgs),
                                                 ctypes.POINTER(DsaidxRope), P]),
-                           ("dsaidx_mqa_logits", [ctypes.POINTER(DsaidxLogitsArgs), P])):
+                           ("dsaidx_mqa_logits", [ctypes.POINTER(DsaidxLogitsArgs), P]),
+                           ("dsaidx_proj_k_norm_rope_quant_store",
+                            [ctypes.POINTER(DsaidxProjArgs), ctypes.POINTER(DsaidxKArgs),
+                             ctypes.POINTER(DsaidxRope), P])):
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -120,7 +133,8 @@ def lib() -> ctypes.CDLL:
         L.dsaidx_abi_version.restype = ctypes.c_int
         L.dsaidx_struct_size.argtypes = [ctypes.c_int]
         L.dsaidx_struct_size.restype = ctypes.c_size_t
-        for which, cls in enumerate((DsaidxRope, DsaidxQArgs, DsaidxKArgs, DsaidxLogitsArgs)):
+        for which, cls in enumerate((DsaidxRope, DsaidxQArgs, DsaidxKArgs, DsaidxLogitsArgs,
+                                     DsaidxProjArgs)):
             if L.dsaidx_struct_size(which) != ctypes.sizeof(cls):
                 raise RuntimeError("libdsaidx ABI mismatch for %s" % cls.__name__)
         _lib = L
@@ -175,6 +189,13 @@ def dsaidx_k_norm_rope_quant_store(k: DsaidxKArgs, rope: DsaidxRope, stream=None
 def dsaidx_qk_fused(q: DsaidxQArgs, k: DsaidxKArgs, rope: DsaidxRope, stream=None) -> None:
     _check(lib().dsaidx_qk_fused(ctypes.byref(q), ctypes.byref(k), ctypes.byref(rope),
                                  _stream_handle(stream)), "dsaidx_qk_fused")
+
+
+def dsaidx_proj_k_norm_rope_quant_store(proj: "DsaidxProjArgs", k: DsaidxKArgs, rope: DsaidxRope,
+                                        stream=None) -> None:
+    _check(lib().dsaidx_proj_k_norm_rope_quant_store(ctypes.byref(proj), ctypes.byref(k),
+                                                     ctypes.byref(rope), _stream_handle(stream)),
+           "dsaidx_proj_k_norm_rope_quant_store")
 
 
 def dsaidx_k_only_prepare_store(k: DsaidxKArgs, rope: DsaidxRope, stream=None) -> None:
@@ -348,7 +369,8 @@ def q_args(q, weights, positions, q_fp8, weights_out, q_scale_out=None,
 
 def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cache,
            k_scale=None, flags: int = 0, page_size: int = 0, num_slots=None) -> DsaidxKArgs:
-    """k: bf16 [T, 128] (unit inner stride); ln_gamma/ln_beta float32 [128];
+    """k: bf16 [T, 128] (unit inner stride), or None for the projection entry
+    (T is then the length of positions); ln_gamma/ln_beta float32 [128];
     positions/out_cache_loc int64 [T].
 
     Planar cache (default): k_cache 1-byte [S, >=128] (unit inner stride;
@@ -361,9 +383,12 @@ def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cach
     import torch
     _on_device(k=k, ln_gamma=ln_gamma, ln_beta=ln_beta, positions=positions,
                out_cache_loc=out_cache_loc, k_cache=k_cache, k_scale=k_scale)
-    _need(k.dtype == torch.bfloat16 and k.dim() == 2 and k.shape[1] == ROW and k.stride(1) == 1,
-          "k must be bf16 [T, 128] with unit inner stride")
-    T = k.shape[0]
+    if k is None:   # the projection entry computes the key itself
+        T = positions.numel()
+    else:
+        _need(k.dtype == torch.bfloat16 and k.dim() == 2 and k.shape[1] == ROW and k.stride(1) == 1,
+              "k must be bf16 [T, 128] with unit inner stride")
+        T = k.shape[0]
     for name, t in (("ln_gamma", ln_gamma), ("ln_beta", ln_beta)):
         _need(t.dtype == torch.float32 and t.numel() == ROW and t.is_contiguous(),
               "%s must be contiguous float32 [128]" % name)
@@ -383,9 +408,34 @@ def k_args(k, ln_gamma, ln_beta, ln_eps: float, positions, out_cache_loc, k_cach
         _need(k_scale is not None and k_scale.dtype == torch.float32 and k_scale.numel() == S
               and k_scale.is_contiguous(), "k_scale must be contiguous float32 [S]")
         row_stride, scale_ptr = k_cache.stride(0), _ptr(k_scale)
-    return DsaidxKArgs(_ptr(k), k.stride(0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps),
+    return DsaidxKArgs(_ptr(k), k.stride(0) if k is not None else ROW, _ptr(ln_gamma), _ptr(ln_beta),
+                       float(ln_eps),
                        int(flags), _ptr(positions), _ptr(out_cache_loc), T, _ptr(k_cache),
                        row_stride, scale_ptr, S, int(page_size))
+
+
+def proj_args(hidden, weight, gates_out, k_out=None) -> DsaidxProjArgs:
+    """hidden: bf16 [T, d] with unit inner stride; weight: bf16 [128 + H, d]
+    with unit inner stride (a Linear layer's [out, in] layout); gates_out:
+    bf16 [T, H] with unit inner stride; k_out: bf16 [T, 128] with unit inner
+    stride, or None."""
+    import torch
+    _on_device(hidden=hidden, weight=weight, gates_out=gates_out, k_out=k_out)
+    _need(hidden.dtype == torch.bfloat16 and hidden.dim() == 2 and hidden.stride(1) == 1,
+          "hidden must be bf16 [T, d] with unit inner stride")
+    T, d = hidden.shape
+    _need(weight.dtype == torch.bfloat16 and weight.dim() == 2 and weight.shape[1] == d
+          and weight.shape[0] > ROW and weight.stride(1) == 1,
+          "weight must be bf16 [128 + H, d] with unit inner stride")
+    H = weight.shape[0] - ROW
+    _need(gates_out.dtype == torch.bfloat16 and tuple(gates_out.shape) == (T, H)
+          and gates_out.stride(1) == 1, "gates_out must be bf16 [T, H] with unit inner stride")
+    if k_out is not None:
+        _need(k_out.dtype == torch.bfloat16 and tuple(k_out.shape) == (T, ROW) and k_out.stride(1) == 1,
+              "k_out must be bf16 [T, 128] with unit inner stride")
+    return DsaidxProjArgs(_ptr(hidden), hidden.stride(0) if T else d, _ptr(weight), weight.stride(0), d,
+                          H, 0, _ptr(gates_out), gates_out.stride(0) if T else H, _ptr(k_out),
+                          k_out.stride(0) if (k_out is not None and T) else ROW)
 
 
 def logits_args(q_fp8, weights, k_cache, logits, k_scale=None, key_slots=None, lengths=None,

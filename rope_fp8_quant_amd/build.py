@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(PKG, "libdsaidx.so")
 ARCH = "gfx950"
 
 SOURCES = ["dsaidx_kernels.hip", "dsaidx_topk.hip", "dsaidx_logits.hip", "dsaidx_hbm_ref.hip",
-           "dsaidx_api.cpp"]
-HEADERS = [os.path.join(INCLUDE, "dsaidx.h"), os.path.join(CSRC, "dsaidx_internal.h")]
+           "dsaidx_proj.hip", "dsaidx_api.cpp"]
+HEADERS = [os.path.join(INCLUDE, "dsaidx.h"), os.path.join(CSRC, "dsaidx_internal.h"),
+           os.path.join(CSRC, "dsaidx_prep_device.h")]
 
 
 def hipcc() -> str:

@@ -76,13 +76,16 @@ dsaidx_status check_q(const dsaidx_q_args* q) {
     return DSAIDX_OK;
 }
 
-dsaidx_status check_k(const dsaidx_k_args* k) {
-    if (!k->k || !k->ln_gamma || !k->ln_beta || !k->positions || !k->out_cache_loc || !k->k_cache)
+// The key side; with_row = false skips k and k_stride_t (the projection entry
+// computes the key itself).
+dsaidx_status check_k(const dsaidx_k_args* k, bool with_row = true) {
+    if (!k->ln_gamma || !k->ln_beta || !k->positions || !k->out_cache_loc || !k->k_cache)
         return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (!aligned(k->k, 16) || !aligned(k->ln_gamma, 16) || !aligned(k->ln_beta, 16) ||
-        !aligned(k->positions, 8) || !aligned(k->out_cache_loc, 8) || !aligned(k->k_cache, 8))
+    if (!aligned(k->ln_gamma, 16) || !aligned(k->ln_beta, 16) || !aligned(k->positions, 8) ||
+        !aligned(k->out_cache_loc, 8) || !aligned(k->k_cache, 8))
         return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (k->k_stride_t < dsaidx::kRow || k->k_stride_t % 8 != 0) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (with_row && (!k->k || !aligned(k->k, 16) || k->k_stride_t < dsaidx::kRow || k->k_stride_t % 8 != 0))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
     if (!(k->ln_eps > 0.0f) || !std::isfinite(k->ln_eps)) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (k->flags & ~(DSAIDX_K_BF16_INTERMEDIATE | DSAIDX_K_PAGED_CACHE | DSAIDX_K_BF16_ROUND_ONCE))
         return DSAIDX_ERR_INVALID_ARGUMENT;
@@ -283,6 +286,50 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     return launch(p, rope->style, qb + kb, kBlock, stream);
 }
 
+dsaidx_status dsaidx_proj_k_norm_rope_quant_store(const dsaidx_proj_args* j, const dsaidx_k_args* k,
+                                                  const dsaidx_rope* rope, dsaidx_stream_t stream) {
+    if (!j || !k || !rope || !token_count_ok(k->num_tokens)) return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (k->num_tokens == 0) return DSAIDX_OK;
+    dsaidx_status st = check_rope(rope);
+    if (st == DSAIDX_OK) st = check_k(k, false);
+    if (st != DSAIDX_OK) return st;
+    const int64_t d = j->hidden_dim;
+    if (d < dsaidx::kProjStageK || d > (int64_t(1) << 20) || d % dsaidx::kProjStageK != 0)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (j->num_heads < 1 || j->num_heads > dsaidx::kProjMaxHeads || j->reserved != 0)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!j->hidden || !aligned(j->hidden, 16) || j->hidden_stride_t < d || j->hidden_stride_t % 8 != 0)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!j->weight || !aligned(j->weight, 16) || j->weight_stride_n < d || j->weight_stride_n % 8 != 0)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (!j->gates_out || !aligned(j->gates_out, 2) || j->gates_stride_t < j->num_heads)
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    if (j->k_out && (!aligned(j->k_out, 16) || j->k_out_stride_t < dsaidx::kRow ||
+                     j->k_out_stride_t % 8 != 0))
+        return DSAIDX_ERR_INVALID_ARGUMENT;
+    dsaidx::ProjParams p;
+    std::memset(&p, 0, sizeof p);
+    fill_rope(p.prep, *rope);
+    fill_k(p.prep, *k);
+    p.prep.k = nullptr;
+    p.prep.k_st = 0;
+    p.x = j->hidden;
+    p.x_st = j->hidden_stride_t;
+    p.w = j->weight;
+    p.w_st = j->weight_stride_n;
+    p.d = (int32_t)d;
+    p.H = j->num_heads;
+    p.n_out = dsaidx::kRow + j->num_heads;
+    p.gates = j->gates_out;
+    p.g_st = j->gates_stride_t;
+    p.k_out = j->k_out;
+    p.ko_st = j->k_out_stride_t;
+    p.row_blocks = ceil_div(k->num_tokens, dsaidx::kProjRows);
+    const int64_t grid = p.row_blocks < max_grid(256) ? p.row_blocks : max_grid(256);
+    return to_status(dsaidx::launch_proj(p, rope->style, (unsigned)grid,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 static bool topk_shape_ok(int64_t rows, int64_t cols, int32_t k) {
     return rows >= 0 && rows < (int64_t(1) << 31) && cols >= 0 && cols < (int64_t(1) << 31) &&
            k >= 1 && k <= (1 << 20);
@@ -450,6 +497,7 @@ size_t dsaidx_struct_size(int which) {
         case 1: return sizeof(dsaidx_q_args);
         case 2: return sizeof(dsaidx_k_args);
         case 3: return sizeof(dsaidx_logits_args);
+        case 4: return sizeof(dsaidx_proj_args);
     }
     return 0;
 }

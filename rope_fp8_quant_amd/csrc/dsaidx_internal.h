@@ -96,6 +96,33 @@ hipError_t topk_scratch(int device, void** ptr);
 hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, float scale,
                                unsigned grid, hipStream_t stream);
 
+// Fused key / head-gate projection with the key preparation in its epilogue
+// (one dispatch): out = hidden [T, d] x W[128 + H, d]^T in fp32 on the matrix
+// cores, rounded to bf16; columns 0..127 go through the key preparation of
+// `prep` (its k / k_st are unused), columns 128.. are written to gates.
+constexpr int kProjRows = 128;       // tokens per workgroup
+constexpr int kProjMaxHeads = 64;    // gate columns at most
+constexpr int kProjMaxCols = kRow + kProjMaxHeads;
+constexpr int kProjStageK = 64;      // d is a multiple of this
+
+struct ProjParams {
+    const uint16_t* x;     // hidden bf16 [T, d], token stride x_st (elements)
+    int64_t x_st;
+    const uint16_t* w;     // weight bf16 [n_out, d], row stride w_st (elements)
+    int64_t w_st;
+    int32_t d;
+    int32_t n_out;         // 128 + H
+    int32_t H;
+    uint16_t* gates;       // bf16 [T, H], token stride g_st
+    int64_t g_st;
+    uint16_t* k_out;       // bf16 [T, 128] (token stride ko_st) or null
+    int64_t ko_st;
+    int64_t row_blocks;    // ceil(T / kProjRows)
+    PrepParams prep;       // the key side and the rope table
+};
+
+hipError_t launch_proj(const ProjParams& p, int style, unsigned grid, hipStream_t stream);
+
 // Reference HBM stream over `vectors` 16-byte vectors: mode 0 copy, 1 read,
 // 2 write (one dispatch).
 hipError_t launch_hbm_stream(int mode, const void* src, void* dst, int64_t vectors,

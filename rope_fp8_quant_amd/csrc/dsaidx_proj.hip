@@ -1,0 +1,221 @@
+// gfx950 kernel of the fused key / head-gate projection with the key
+// preparation in its epilogue.
+//
+// The indexer computes its key and its head gates with one projection of the
+// hidden states, the fused wk_weights_proj GEMM ([sglang-fuse] Motivation):
+//   out[t, n] = sum_c hidden[t, c] * W[n, c],   n < 128: the key,
+//                                              128 <= n < 128 + H: the gates.
+// The unfused path writes out as bf16 and the preparation reads it back.  Here
+// one dispatch does both: the projection on the matrix cores, then, while the
+// workgroup's 128 key rows are still on chip, their LayerNorm, RoPE,
+// quantisation and index-K cache store (the same device code as the key rows
+// of the preparation kernel), and the gates written as bf16 for the query-side
+// call.  The key values are rounded to bf16 first, as the GEMM's output is, so
+// the cache holds what the preparation would store from that output.
+//
+// Mapping.  A workgroup of four wavefronts owns 128 tokens and all 128 + H
+// (at most 192) output columns; wavefront w owns tokens 32w .. 32w + 31 as two
+// 16-row blocks.  The contraction runs in stages of 64 hidden elements with
+// v_mfma_f32_16x16x32_bf16 (A: 16 tokens x 32, B: 32 x 16 columns):
+//   - hidden rows go straight from HBM into the A operands (16 bytes per lane,
+//     lane l: token l % 16, elements 8 (l / 16) ..), nontemporal: every
+//     element is read once;
+//   - the stage's weight slice (192 rows x 128 bytes) goes through LDS,
+//     double-buffered, one barrier per stage; its rows are 144 bytes apart so
+//     that the 16 lanes of a B-operand read hit distinct banks;
+//   - each wavefront issues 2 x 12 MFMAs per 32 elements, accumulating in
+//     fp32.
+// The next stage's loads are issued before the current stage's MFMAs.  The
+// call is bound by the hidden states' HBM traffic: the weight (0.3 % of the
+// bytes at d = 7168) is re-read from L2 by every workgroup.
+#include "dsaidx_prep_device.h"
+
+#pragma clang fp contract(off)
+
+namespace dsaidx {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kColBlocks = kProjMaxCols / 16;        // 12 blocks of 16 output columns
+constexpr int kStageK = 64;                          // hidden elements per stage
+constexpr int kWPitch = kStageK * 2 + 16;            // LDS bytes per weight row (144)
+constexpr int kWStageBytes = kProjMaxCols * kWPitch;   // 27648
+constexpr int kKPitch = kRow * 2 + 16;               // LDS bytes per staged key row (272)
+constexpr int kGPitch = kProjMaxHeads * 2 + 16;      // LDS bytes per staged gate row (144)
+static_assert(kProjRows * (kKPitch + kGPitch) <= 2 * kWStageBytes, "epilogue staging fits the stages");
+static_assert(kProjRows == 32 * (kThreads / 64), "32 tokens per wavefront");
+
+// The lane's eight bf16 values of one staged key row (layout order), from LDS.
+template <int LAYOUT>
+__device__ __forceinline__ uint4 lds_row(const uint8_t* row, int j) {
+    if (LAYOUT != kSplit) return *reinterpret_cast<const uint4*>(row + 16 * j);
+    const uint2 a = *reinterpret_cast<const uint2*>(row + 8 * j);
+    const uint2 b = *reinterpret_cast<const uint2*>(row + 128 + 8 * j);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+__device__ __forceinline__ uint4 load16_keep(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+template <int STYLE, int LAYOUT>
+__global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a) {
+    __shared__ __align__(16) uint8_t smem[2 * kWStageBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15;          // MFMA operand row / column within a block
+    const int lq = lane >> 4;          // MFMA operand k group (8 elements)
+    const int wc = tid & 7;            // weight staging: 16-byte chunk of a row's stage slice
+    const int wr0 = tid >> 3;          //   and first row (rows wr0 + 32 j)
+    const int64_t T = a.prep.T;
+    const int stages = a.d / kStageK;
+
+    for (int64_t blk = blockIdx.x; blk < a.row_blocks; blk += gridDim.x) {
+        const int64_t row0 = blk * kProjRows;
+        const uint16_t* arow[2];
+        bool aval[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t = row0 + 32 * wave + 16 * i + lr;
+            aval[i] = t < T;
+            arow[i] = a.x + (aval[i] ? t : 0) * a.x_st + 8 * lq;
+        }
+        f32x4 acc[2][kColBlocks];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int cb = 0; cb < kColBlocks; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        uint4 wreg[6], areg[2][2];
+        auto load_stage = [&](int s, uint4 (&w)[6], uint4 (&x)[2][2]) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    x[i][ks] = aval[i] ? load16(arow[i] + s * kStageK + 32 * ks) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int jj = 0; jj < 6; ++jj) {
+                const int n = wr0 + 32 * jj;
+                w[jj] = n < a.n_out ? load16_keep(a.w + (int64_t)n * a.w_st + s * kStageK + 8 * wc)
+                                    : make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto store_stage = [&](int buf, const uint4 (&w)[6]) {
+            uint8_t* base = smem + buf * kWStageBytes + 16 * wc;
+#pragma unroll
+            for (int jj = 0; jj < 6; ++jj)
+                *reinterpret_cast<uint4*>(base + (wr0 + 32 * jj) * kWPitch) = w[jj];
+        };
+
+        load_stage(0, wreg, areg);
+        store_stage(0, wreg);
+        __syncthreads();
+        for (int s = 0; s < stages; ++s) {
+            uint4 wnext[6], anext[2][2];
+            const bool more = s + 1 < stages;
+            if (more) load_stage(s + 1, wnext, anext);
+            const uint8_t* wb = smem + (s & 1) * kWStageBytes + lr * kWPitch + 16 * lq;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, areg[0][ks]);
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, areg[1][ks]);
+#pragma unroll
+                for (int cb = 0; cb < kColBlocks; ++cb) {
+                    const bf16x8 b = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4*>(wb + cb * 16 * kWPitch + 64 * ks));
+                    acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][cb], 0, 0, 0);
+                    acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][cb], 0, 0, 0);
+                }
+            }
+            if (more) {
+                store_stage((s + 1) & 1, wnext);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    areg[i][0] = anext[i][0];
+                    areg[i][1] = anext[i][1];
+                }
+            }
+            __syncthreads();
+        }
+
+        // Epilogue 1: the projection's output rounded to bf16 (nearest even),
+        // staged in LDS (the stage buffers are free): key rows [128][128] and
+        // gate rows [128][H].  Lane l holds column l % 16 of rows 4 (l / 16) ..
+        // + 3 of each 16 x 16 block.
+        uint8_t* ktile = smem;
+        uint8_t* gtile = smem + kProjRows * kKPitch;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int cb = 0; cb < kColBlocks; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 32 * wave + 16 * i + 4 * lq + e;
+                    const int c = 16 * cb + lr;
+                    const uint16_t v = (uint16_t)(__float_as_uint(round_bf16(acc[i][cb][e])) >> 16);
+                    if (c < kRow)
+                        *reinterpret_cast<uint16_t*>(ktile + r * kKPitch + 2 * c) = v;
+                    else if (c - kRow < a.H)
+                        *reinterpret_cast<uint16_t*>(gtile + r * kGPitch + 2 * (c - kRow)) = v;
+                }
+        __syncthreads();
+
+        // Epilogue 2: the gates (and, when asked, the bf16 key) to HBM.
+        const int rows_here = (int)(T - row0 < kProjRows ? T - row0 : kProjRows);
+        for (int idx = tid; idx < rows_here * a.H; idx += kThreads) {
+            const int r = idx / a.H;
+            const int h = idx - r * a.H;
+            a.gates[(row0 + r) * a.g_st + h] = *reinterpret_cast<const uint16_t*>(gtile + r * kGPitch + 2 * h);
+        }
+        if (a.k_out) {
+            for (int idx = tid; idx < rows_here * 16; idx += kThreads) {
+                const int r = idx >> 4;
+                const int c = idx & 15;
+                *reinterpret_cast<uint4*>(a.k_out + (row0 + r) * a.ko_st + 8 * c) =
+                    *reinterpret_cast<const uint4*>(ktile + r * kKPitch + 16 * c);
+            }
+        }
+
+        // Epilogue 3: the key rows, four per wavefront pass, through the
+        // preparation's key-row code (LayerNorm, RoPE, quantisation, store).
+        const int g = lane >> 4;
+        const int j = lane & (kLanesPerRow - 1);
+        for (int pass = 0; pass < 8; ++pass) {
+            const int r = 32 * wave + 4 * pass + g;
+            const int64_t t = row0 + r;
+            const bool valid = t < T;
+            const uint4 raw = lds_row<LAYOUT>(ktile + r * kKPitch, j);
+            int64_t pos = 0, slot = -1;
+            if (valid) {
+                pos = clamp_position(a.prep.k_pos[t], a.prep.P);
+                slot = a.prep.loc[t];
+            }
+            key_row<STYLE, LAYOUT>(a.prep, valid, raw, pos, slot, lane);
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj(const ProjParams& p, int style, unsigned grid, hipStream_t stream) {
+    ProjParams copy = p;
+    void* args[] = {&copy};
+    const void* fn;
+    if (p.prep.generic)
+        fn = style == 1 ? reinterpret_cast<const void*>(&proj_key_prep_kernel<1, kGeneric>)
+                        : reinterpret_cast<const void*>(&proj_key_prep_kernel<0, kGeneric>);
+    else if (style == 1)
+        fn = reinterpret_cast<const void*>(&proj_key_prep_kernel<1, kSplit>);
+    else if (p.prep.R <= 64)
+        fn = reinterpret_cast<const void*>(&proj_key_prep_kernel<0, kSplit>);
+    else
+        fn = reinterpret_cast<const void*>(&proj_key_prep_kernel<0, kContig>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace dsaidx

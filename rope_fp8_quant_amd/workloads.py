@@ -233,6 +233,53 @@ def bytes_per_call(T: int, H: int = 64, entry: str = "fused", rope_dim: int = 64
     return T * bytes_per_token(H, entry, rope_dim) + per_call
 
 
+# ---------------------------------------- key / head-gate projection ----
+
+@dataclass
+class ProjWorkload:
+    """Inputs of the key / head-gate projection with the key preparation in
+    its epilogue: hidden states and the projection weight, plus the key side
+    (positions, slots, LayerNorm parameters, rope table) of `key`, a Workload
+    whose q / k / weights are not used."""
+    name: str
+    T: int
+    d: int
+    H: int
+    hidden: np.ndarray      # uint16 (bf16 bits) [T, d]
+    weight: np.ndarray      # uint16 (bf16 bits) [128 + H, d]
+    key: Workload
+
+
+def proj_make(T: int, d: int = 7168, H: int = 64, *, seed: int = 0, name: str = "custom",
+              **key_kw) -> ProjWorkload:
+    """Hidden states N(0,1) and weight N(0, 1/d), both rounded to bf16, so each
+    projected value is about N(0,1); the key side from make(T, H, ...) with
+    key_kw (positions, slots, table, rope) and the same seed.  The pages give
+    no hidden size; d = 7168 is the hidden width of the DeepSeek-V3 family whose
+    sparse-attention indexer the pages run."""
+    kids = np.random.SeedSequence(seed).spawn(2)
+    rh, rw = (np.random.default_rng(s) for s in kids)
+    hidden = _draw_values(rh, (T, d), "normal", chunk_rows=max(1, (1 << 24) // d))
+    weight = f32_to_bf16_bits(rw.standard_normal((ROW + H, d), dtype=np.float32)
+                              * np.float32(1.0 / np.sqrt(d)))
+    key = make(min(T, 1) if T == 0 else T, H=1, seed=seed, name=name + "_key", **key_kw)
+    return ProjWorkload(name=name, T=T, d=d, H=H, hidden=hidden, weight=weight, key=key)
+
+
+def proj_bytes_per_call(T: int, d: int = 7168, H: int = 64, rope_dim: int = 64) -> int:
+    """Algorithmic HBM bytes of one projection call: hidden [T, d] and weight
+    [128 + H, d] bf16 read once, the key side's reads (position, slot, cos/sin
+    row per token; gamma and beta once) and writes (code row and scale), and
+    the gates written as bf16 [T, H]."""
+    key_side = T * (8 + 8 + 2 * (rope_dim // 2) * 4 + ROW + 4) + 2 * ROW * 4
+    return T * d * 2 + (ROW + H) * d * 2 + key_side + T * H * 2
+
+
+def proj_flops_per_call(T: int, d: int = 7168, H: int = 64) -> int:
+    """2 * T * d * (128 + H): one multiply and one add per term."""
+    return 2 * T * d * (ROW + H)
+
+
 # ------------------------------------------------ top-k per row inputs ----
 
 @dataclass

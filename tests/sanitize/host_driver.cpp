@@ -15,7 +15,7 @@
 namespace {
 
 struct Launch {
-    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test, 3 logits, 4 HBM stream
+    int kind;  // 0 prep, 1 top-k, 2 fp8 self-test, 3 logits, 4 HBM stream, 5 projection
     dsaidx::PrepParams p;
     dsaidx::LogitsParams lp;
     int style;
@@ -88,6 +88,22 @@ hipError_t launch_logits(const LogitsParams& p, hipStream_t) {
     std::memset(&l, 0, sizeof l);
     l.kind = 3;
     l.lp = p;
+    g_launches.push_back(l);
+    return g_fail;
+}
+
+hipError_t launch_proj(const ProjParams& p, int style, unsigned grid, hipStream_t) {
+    Launch l;
+    std::memset(&l, 0, sizeof l);
+    l.kind = 5;
+    l.p = p.prep;
+    l.style = style;
+    l.grid = grid;
+    l.n = p.d;
+    l.rows = p.row_blocks;
+    l.k = p.H;
+    l.row_stride = p.x_st;
+    l.workspace = p.k_out;
     g_launches.push_back(l);
     return g_fail;
 }
@@ -641,8 +657,65 @@ void logits_calls() {
     });
 }
 
+// The projection entry: one dispatch of ceil(T / 128) workgroups, the key
+// side filled as for the key entry (its row pointer unused), every rejected
+// argument enqueuing nothing.
+void projection_calls() {
+    dsaidx_rope rope = make_rope();
+    auto proj = [](int64_t d, int32_t H) {
+        dsaidx_proj_args j;
+        std::memset(&j, 0, sizeof j);
+        j.hidden = at<const uint16_t>(1 << 20);
+        j.hidden_stride_t = d;
+        j.weight = at<const uint16_t>(1 << 22);
+        j.weight_stride_n = d;
+        j.hidden_dim = d;
+        j.num_heads = H;
+        j.gates_out = at<uint16_t>(1 << 24);
+        j.gates_stride_t = H;
+        return j;
+    };
+    dsaidx_k_args k = make_k(300);
+    k.k = nullptr;
+    k.k_stride_t = 0;
+    g_launches.clear();
+    dsaidx_proj_args j = proj(7168, 64);
+    CHECK(dsaidx_proj_k_norm_rope_quant_store(&j, &k, &rope, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.size() == 1 && g_launches[0].kind == 5);
+    if (!g_launches.empty()) {
+        const Launch& l = g_launches[0];
+        CHECK(l.grid == 3 && l.rows == 3 && l.n == 7168 && l.k == 64 && l.style == 0);
+        CHECK(l.p.T == 300 && l.p.k == nullptr && l.p.loc == k.out_cache_loc && l.p.S == k.num_slots);
+        CHECK(l.workspace == nullptr);
+    }
+    // T = 0: nothing, whatever the pointers
+    g_launches.clear();
+    dsaidx_k_args k0 = make_k(0);
+    dsaidx_proj_args j0;
+    std::memset(&j0, 0, sizeof j0);
+    CHECK(dsaidx_proj_k_norm_rope_quant_store(&j0, &k0, &rope, nullptr) == DSAIDX_OK);
+    CHECK(g_launches.empty());
+    auto bad = [&](void (*edit)(dsaidx_proj_args&, dsaidx_k_args&)) {
+        dsaidx_proj_args jj = proj(7168, 64);
+        dsaidx_k_args kk = k;
+        edit(jj, kk);
+        REJECT(dsaidx_proj_k_norm_rope_quant_store(&jj, &kk, &rope, nullptr));
+    };
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.hidden_dim = 96; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.hidden_dim = 0; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.num_heads = 65; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.hidden = nullptr; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.weight_stride_n = 7000; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.gates_stride_t = 32; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.k_out = at<uint16_t>(8); j.k_out_stride_t = 128; });
+    bad([](dsaidx_proj_args&, dsaidx_k_args& k) { k.ln_eps = 0.0f; });
+    bad([](dsaidx_proj_args&, dsaidx_k_args& k) { k.k_cache = nullptr; });
+    CHECK(dsaidx_proj_k_norm_rope_quant_store(nullptr, &k, &rope, nullptr) == DSAIDX_ERR_INVALID_ARGUMENT);
+}
+
 int main() {
     abi_and_status();
+    projection_calls();
     logits_calls();
     launch_shapes();
     rejected_arguments();

@@ -46,11 +46,12 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_struct_sizes(L):
-    assert B.dsaidx_abi_version() == 5
+    assert B.dsaidx_abi_version() == 6
     assert L.dsaidx_struct_size(0) == ctypes.sizeof(B.DsaidxRope) == 40
     assert L.dsaidx_struct_size(1) == ctypes.sizeof(B.DsaidxQArgs) == 88
     assert L.dsaidx_struct_size(2) == ctypes.sizeof(B.DsaidxKArgs) == 104
     assert L.dsaidx_struct_size(3) == ctypes.sizeof(B.DsaidxLogitsArgs) == 112
+    assert L.dsaidx_struct_size(4) == ctypes.sizeof(B.DsaidxProjArgs) == 80
     assert L.dsaidx_struct_size(7) == 0
 
 
@@ -339,3 +340,41 @@ def test_binding_refuses_host_tensors(L):
     for make in cases:
         with pytest.raises(ValueError, match="GPU tensor"):
             make()
+
+
+def good_proj(**kw):
+    p = B.DsaidxProjArgs(FAKE, 7168, FAKE, 7168, 7168, 64, 0, FAKE, 64, None, 128)
+    for k_, v in kw.items():
+        setattr(p, k_, v)
+    return p
+
+
+def call_proj(L, p, k, r):
+    return L.dsaidx_proj_k_norm_rope_quant_store(ctypes.byref(p), ctypes.byref(k), ctypes.byref(r), None)
+
+
+BAD_PROJ = [dict(hidden=None), dict(weight=None), dict(gates_out=None), dict(hidden=FAKE + 8),
+            dict(weight=FAKE + 8), dict(gates_out=FAKE + 1), dict(k_out=FAKE + 8),
+            dict(hidden_dim=0), dict(hidden_dim=96), dict(hidden_dim=7168 + 32), dict(hidden_dim=1 << 21),
+            dict(hidden_stride_t=7160), dict(hidden_stride_t=7172), dict(weight_stride_n=7160),
+            dict(weight_stride_n=7172), dict(num_heads=0), dict(num_heads=65), dict(reserved=1),
+            dict(gates_stride_t=63), dict(k_out=FAKE, k_out_stride_t=120),
+            dict(k_out=FAKE, k_out_stride_t=132)]
+
+
+@pytest.mark.parametrize("kw", BAD_PROJ, ids=lambda d: str(d))
+def test_bad_projection_rejected(L, kw):
+    assert call_proj(L, good_proj(**kw), good_k(k=None, k_stride_t=0), good_rope()) == \
+        B.DSAIDX_ERR_INVALID_ARGUMENT
+
+
+def test_projection_checks_key_side_but_not_its_row(L):
+    """The projection computes the key: k and k_stride_t are not looked at,
+    the rest of the key side is checked as for the key entry."""
+    ok = call_proj(L, good_proj(), good_k(k=None, k_stride_t=0), good_rope())
+    assert ok != B.DSAIDX_ERR_INVALID_ARGUMENT          # no GPU here: the launch itself fails
+    assert call_proj(L, good_proj(), good_k(k=None, ln_eps=0.0), good_rope()) == \
+        B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_proj(L, good_proj(), good_k(k=None, out_cache_loc=None), good_rope()) == \
+        B.DSAIDX_ERR_INVALID_ARGUMENT
+    assert call_proj(L, good_proj(hidden=None), good_k(T=0), good_rope()) == B.DSAIDX_OK

@@ -1,4 +1,5 @@
-"""Planted mistakes in the Python oracles (index logits, top-k per row) must
+"""Planted mistakes in the Python oracles (index logits, top-k per row, the
+key / head-gate projection) must
 fail their pins (CPU only).
 
 Each case copies the oracle module's source, plants one plausible mistake (a
@@ -20,6 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 LOGITS = ("oracle/logits.py", "logits", "tests/test_oracle_logits.py")
 TOPK = ("oracle/topk.py", "topk", "tests/test_oracle_topk.py")
+PROJ = ("oracle/proj.py", "proj", "tests/test_oracle_proj.py")
 
 MUTANTS = [
     ("logits_relu_after_head_sum", LOGITS,
@@ -45,6 +47,20 @@ MUTANTS = [
     ("topk_takes_one_less", TOPK, "take = min(n, k)", "take = min(n, k - 1) if n > k else min(n, k)"),
     ("topk_length_off_by_one", TOPK, "v = np.sort(logits[r, :n])[::-1]",
      "v = np.sort(logits[r, :n + 1])[::-1]"),
+    ("proj_key_gate_split_swapped", PROJ,
+     "return np.ascontiguousarray(bits[:, :ROW]), np.ascontiguousarray(bits[:, ROW:])",
+     "return np.ascontiguousarray(bits[:, -ROW:]), np.ascontiguousarray(bits[:, :-ROW])"),
+    ("proj_round_half_up", PROJ, "q = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
+     "q = np.ldexp(np.floor(np.ldexp(m, 8) + 0.5), e - 8)"),
+    ("proj_truncates", PROJ, "q = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
+     "q = np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)"),
+    ("proj_seven_bits", PROJ, "q = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
+     "q = np.ldexp(np.rint(np.ldexp(m, 7)), e - 7)"),
+    ("proj_rounds_through_fp32", PROJ, "    x = np.asarray(x, dtype=np.float64)\n",
+     "    x = np.asarray(x, dtype=np.float32).astype(np.float64)\n"),
+    ("proj_weight_transposed", PROJ, "return x @ w.T, np.abs(x) @ np.abs(w).T",
+     "return (x.T[:w.shape[0]].T @ w[:, :x.shape[0]].T[:x.shape[1]] if x.shape[0] == w.shape[1] "
+     "else x[:, ::-1] @ w.T), np.abs(x) @ np.abs(w).T"),
 ]
 
 PLUGIN = textwrap.dedent('''
