@@ -4,9 +4,10 @@ Tolerance, from the arithmetic of the matrix unit.  Every product of two E4M3
 values is exact, but v_mfma_f32_16x16x128_f8f6f4 does not add the 128
 products of a dot in IEEE fp32: it aligns them to the largest one and keeps a
 limited number of bits, so its error scales with the largest product of the
-dot (a probe of 51200 dots of random full-range codes on MI355X found at most
-2^-10.65 of the largest product's binade, no sign bias, and exact results when
-all codes share a binade).  The gate multiply and the 64-term head sum are
+dot (test_matrix_unit_dot_error below measures this on 51200 dots of random
+full-range codes and asserts the allowance: on MI355X the worst seen was
+2^-10.65 of the largest product, with no sign bias, and dots whose codes share
+a binade came out exact).  The gate multiply and the 64-term head sum are
 ordinary fp32.  The test allows, per entry,
 
   |got - want| <= k_scale * sum_h |w[t, h]| * (2^-8 * max_d |q[t, h, d]| * max_d |k[s, d]|
@@ -292,3 +293,49 @@ def test_named_workloads_sampled_rows(idx):
         assert np.all(err <= tol[:n]), (r, float(np.max(err / tol[:n])))
         worst = max(worst, float(np.max(err / tol[:n])) if n else 0.0)
     print("[parity] %s rows %s: max err / bound %.3g" % (lw.name, rows, worst), flush=True)
+
+
+def test_matrix_unit_dot_error():
+    """The evidence behind the tolerance above: the device's 128-term fp8 dots
+    through dsaidx_mqa_logits itself.  One head, gate 1 and key scale 1 make
+    each logit relu(dot); the same keys with every sign bit flipped give
+    relu(-dot), so the difference is the signed dot as the kernel computes it.
+    Over 51200 dots of random full-range codes (400 tokens x 128 keys), the
+    error against the exact dot (float64 over the decoded codes: each product
+    has at most 8 significant bits, so 128 of them sum exactly) is reported as
+    a fraction of the dot's largest |product|, and must stay within the 2^-8
+    the tolerance allows (of a bound on that product).  Codes that share one
+    binade must give exact dots."""
+    rng = np.random.default_rng(6061)
+    T, N = 400, 128
+    q8, _ = random_query(T, 1, rng)
+    codes, _ = random_cache(N, rng)
+    w = np.ones((T, 1), np.float32)
+    scale = np.ones(N, np.float32)
+    pos = run(q8, w, codes, scale)
+    neg = run(q8, w, codes ^ np.uint8(0x80), scale)
+    got = pos.astype(np.float64) - neg.astype(np.float64)
+    dec = LG.decode_table()
+    qv = dec[q8[:, 0, :]]                       # [T, 128]
+    kv = dec[codes[:, :128]]                    # [N, 128]
+    exact = qv @ kv.T
+    largest = np.abs(qv)[:, None, :] * np.abs(kv)[None, :, :]
+    largest = largest.max(axis=2)
+    err = np.abs(got - exact)
+    nz = largest > 0
+    ratio = np.zeros_like(err)
+    ratio[nz] = err[nz] / largest[nz]
+    worst = float(ratio.max())
+    bias = float(np.mean(np.sign(got - exact)[err > 0])) if np.any(err > 0) else 0.0
+    # one binade: codes with the same exponent field (here 0x40..0x47 and signs)
+    q1 = (0x40 | rng.integers(0, 8, size=(T, 1, 128)) | (rng.integers(0, 2, size=(T, 1, 128)) << 7)).astype(np.uint8)
+    k1 = (0x40 | rng.integers(0, 8, size=(N, 128)) | (rng.integers(0, 2, size=(N, 128)) << 7)).astype(np.uint8)
+    g1 = run(q1, w, k1, scale).astype(np.float64) - run(q1, w, k1 ^ np.uint8(0x80), scale).astype(np.float64)
+    e1 = dec[q1[:, 0, :]] @ dec[k1].T
+    rep = dict(dots=int(err.size), worst_err_over_largest_product=worst,
+               log2_worst=float(np.log2(worst)) if worst > 0 else None,
+               dots_with_error=int(np.count_nonzero(err)), sign_bias=bias,
+               one_binade_max_abs_err=float(np.max(np.abs(g1 - e1))))
+    print("\n[parity] mfma fp8 dot error %s" % json.dumps(rep), flush=True)
+    assert worst <= 2.0 ** -8, rep
+    assert np.array_equal(g1, e1), rep

@@ -176,6 +176,8 @@ CASES = [
     (1000, 256, 33, 96, W.NEOX, R.DSAIDX_K_PAGED_CACHE, 16),
     (2053, 512, 64, 64, W.NEOX, R.DSAIDX_K_BF16_ROUND_ONCE, 0),
     (513, 320, 64, 24, W.INTERLEAVED, R.DSAIDX_K_BF16_INTERMEDIATE, 0),
+    (260, 320, 16, 64, W.NEOX, 0, 0),
+    (131, 448, 64, 64, W.NEOX, 0, 0),
     (700, 1024, 1, 128, W.NEOX, 0, 0),
 ]
 
