@@ -132,11 +132,7 @@ hipError_t launch_hbm_stream(int mode, const void* src, void* dst, int64_t vecto
 // against num_keys keys of the index-K cache.
 constexpr int kLogitsMaxHeads = 64;
 constexpr int kLogitsTokensPerBlock = 8;     // query tokens per workgroup
-#ifndef DSAIDX_LG_KEYS_PER_THREAD
-#define DSAIDX_LG_KEYS_PER_THREAD 2
-#endif
-constexpr int kLogitsKeysPerThread = DSAIDX_LG_KEYS_PER_THREAD;   // key rows each thread stages
-constexpr int kLogitsStageKeys = 64 * kLogitsKeysPerThread;       // keys per LDS stage; chunks are multiples
+constexpr int kLogitsStageKeys = 128;       // keys per LDS stage; chunks are multiples
 
 struct LogitsParams {
     const uint8_t* q;          // [T, H, 128] E4M3 codes
@@ -159,6 +155,7 @@ struct LogitsParams {
     int64_t chunks;            // key chunks: the grid is ceil(T / 8) * chunks
     int32_t chunk_major;       // workgroup order: chunk-major (1) or token-block-major (0)
     int32_t w_vec;             // H % 4 == 0 and weights 16-byte aligned: gates read 4 at a time
+    int32_t tokens_per_wave;   // 1: 8-wavefront workgroups, pipelined blocks; 2: 4 wavefronts
 };
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream);

@@ -15,20 +15,22 @@
 // a 16 (heads) x 16 (keys) block of dots in one instruction.  Products of two
 // E4M3 values are exact in fp32; the 128-term sums and the head sum are fp32.
 //
-// Work: a workgroup of 4 wavefronts takes 8 query tokens (2 per wavefront,
-// their q rows and gates held in registers for the whole call) and one chunk
-// of keys.  Keys are staged through LDS 128 at a time (double-buffered, one
-// barrier per stage; each thread brings 32 bytes of two key rows), so each
-// 16-key block read from L2 feeds 8 tokens x 4 head blocks of MFMAs.  Per
-// block: the 8 MFMAs of a wavefront, the next block's key operand read from
-// LDS behind them, then ReLU and gate on the 4 results of each lane, a sum
-// over the lane groups for both tokens together (two lane-swap instructions),
-// the key scale and one store of 16 keys per token.
+// Work: a workgroup takes 8 query tokens (their q rows and gates held in
+// registers for the whole call) and one chunk of keys: 4 wavefronts of 2
+// tokens, or, for calls whose grid is one resident round (decode), 8
+// wavefronts of 1 token, which hold four wavefronts per SIMD and issue each
+// block's MFMAs before the previous block's epilogue.  Keys are staged
+// through LDS 128 at a time (double-buffered, one barrier per stage; each
+// thread brings 32 bytes of one or two key rows), so each 16-key block read
+// from L2 feeds 8 tokens x 4 head blocks of MFMAs.  Per
+// block (two tokens): the 8 MFMAs of a wavefront, the next block's key
+// operand read from LDS behind them, then ReLU and gate on the 4 results of
+// each lane, a sum over the lane groups for both tokens together (two
+// lane-swap instructions), the key scale and one store of 16 keys per token.
 //
 // Time on gfx950 goes to the matrix unit and the VALU in turn rather than
 // side by side, and the epilogue costs two VALU operations per dot (ReLU and
 // gate FMA): 64 per block and lane, as many cycles as the block's 8 MFMAs.
-// The register budget is held to three wavefronts per SIMD.
 #include "dsaidx_internal.h"
 
 namespace dsaidx {
@@ -37,12 +39,26 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kLgThreads = 256;                   // 4 wavefronts
-constexpr int kLgTokensPerWave = kLogitsTokensPerBlock / 4;
 constexpr int kLgStage = kLogitsStageKeys;        // keys per LDS stage
 constexpr int kLgRowPitch = 144;                  // LDS bytes per staged key row (128 + 16: no bank conflicts)
 constexpr int kLgHeadBlocks = kLogitsMaxHeads / 16;
-static_assert(kLgTokensPerWave == 2, "the lane-group reduction pairs a wavefront's two tokens");
+
+// Workgroup shape for TPW query tokens per wavefront: kLogitsTokensPerBlock
+// tokens per workgroup, so TPW = 2 is 4 wavefronts and TPW = 1 is 8; each
+// thread stages KPT key rows of a stage.  Register budgets: three wavefronts
+// per SIMD for two tokens (168 VGPRs); four for one (128 VGPRs: with the
+// pipelined blocks this leaves no room to read each key operand a block
+// ahead, so one token reads it just before its MFMAs).
+template <int TPW>
+struct LgShape {
+    static_assert(TPW == 1 || TPW == 2, "one or two tokens per wavefront");
+    static constexpr int kWaves = kLogitsTokensPerBlock / TPW;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kKPT = kLgStage / (kThreads / 4);
+    static_assert(kKPT * (kThreads / 4) == kLgStage, "stage rows per thread");
+    static constexpr int kMinWaves = TPW == 2 ? 3 : 4;
+    static constexpr bool kReadAhead = TPW == 2;
+};
 
 // 16 x 16 x 128 block of dots over E4M3 codes (format 0 for both operands,
 // no block scales).  Lane l supplies row l % 16 of A and column l % 16 of B,
@@ -73,11 +89,12 @@ __device__ __forceinline__ int64_t clamp_len(const LogitsParams& p, int64_t t) {
     return l < 0 ? 0 : (l < p.N ? l : p.N);
 }
 
-#ifndef DSAIDX_LG_MIN_WAVES
-#define DSAIDX_LG_MIN_WAVES 3
-#endif
-__global__ __launch_bounds__(kLgThreads) __attribute__((amdgpu_waves_per_eu(DSAIDX_LG_MIN_WAVES)))
+template <int TPW>
+__global__ __launch_bounds__(LgShape<TPW>::kThreads)
+__attribute__((amdgpu_waves_per_eu(LgShape<TPW>::kMinWaves)))
 void mqa_logits_kernel(LogitsParams p) {
+    constexpr int kLgTokensPerWave = TPW;
+    constexpr int TPB = kLogitsTokensPerBlock;
     __shared__ __align__(16) uint8_t kbuf[2][kLgStage * kLgRowPitch];
     __shared__ float kscl[2][kLgStage];
 
@@ -87,7 +104,7 @@ void mqa_logits_kernel(LogitsParams p) {
     const int g = lane >> 4;                      // lane group: bytes [32 g, 32 g + 32)
     // token blocks from the last: under causal lengths the longest rows go
     // first, so the short ones fill in behind them instead of trailing
-    const int64_t nb = (p.T + kLogitsTokensPerBlock - 1) / kLogitsTokensPerBlock;
+    const int64_t nb = (p.T + TPB - 1) / TPB;
     // The 8 XCDs take consecutive workgroups in turn.  Chunk-major order
     // (consecutive workgroups: neighbouring token blocks of one chunk) gives
     // every XCD its share of every chunk whatever the chunk count, which
@@ -104,12 +121,12 @@ void mqa_logits_kernel(LogitsParams p) {
         tb = nb - 1 - bi;
         key0 = (blockIdx.x - bi * p.chunks) * p.chunk;
     }
-    const int64_t t_first = tb * kLogitsTokensPerBlock;
+    const int64_t t_first = tb * TPB;
 
     // keys past every token's length are skipped (the same for the workgroup)
     int64_t kmax = 0;
 #pragma unroll
-    for (int i = 0; i < kLogitsTokensPerBlock; ++i) {
+    for (int i = 0; i < TPB; ++i) {
         const int64_t l = clamp_len(p, t_first + i);
         kmax = l > kmax ? l : kmax;
     }
@@ -154,7 +171,7 @@ void mqa_logits_kernel(LogitsParams p) {
     // into 32-bit registers and widened only when the rows are fetched, so
     // the wavefront does not wait on it in the stage that loads it.
     const int sk = tid >> 2, sp = tid & 3;
-    constexpr int KPT = kLogitsKeysPerThread;
+    constexpr int KPT = LgShape<TPW>::kKPT;
     auto slot_of = [&](int64_t s, int32_t raw) -> int64_t {
         if (s >= kend) return -1;
         return p.key_slots ? (int64_t)raw : s;
@@ -204,22 +221,24 @@ void mqa_logits_kernel(LogitsParams p) {
         }
     };
 
-    // output: after the reduction lanes 0..15 hold token 0's sums and lanes
-    // 32..47 token 1's, for the 16 keys of a block (lane % 16); key offsets
-    // from here on are relative to key0 (below the chunk size, 32-bit)
-    const int oi = lane >> 5;
-    const bool writer = (lane & 16) == 0;
-    const int64_t otok = oi ? tok[1] : tok[0];
-    const int64_t olen = oi ? len[1] : len[0];
+    // output: after the reduction lanes 0..15 hold token 0's sums and (two
+    // tokens) lanes 32..47 token 1's, for the 16 keys of a block (lane % 16);
+    // key offsets from here on are relative to key0 (below the chunk size,
+    // 32-bit)
+    const int oi = TPW == 2 ? lane >> 5 : 0;
+    const bool writer = TPW == 2 ? (lane & 16) == 0 : lane < 16;
+    const int64_t otok = oi ? tok[TPW - 1] : tok[0];
+    const int64_t olen = oi ? len[TPW - 1] : len[0];
     const int64_t ostop = (olen < kend ? olen : kend) - key0;
     const int lim = writer && ostop > 0 ? (int)ostop : 0;     // this lane stores keys rel < lim
     float* const obase = p.out + (otok < p.T ? otok : 0) * p.out_stride + key0;
     const int nkeys = (int)(kend - key0);
 
     // ReLU, gate and head sum of one block's dots, then the sum over the four
-    // lane groups for both tokens at once: the 32-lane swap pairs token 0's
-    // upper half with token 1's lower half, the 16-lane swap then folds the
-    // remaining pair of groups; key scale and store
+    // lane groups: with two tokens, for both at once (the 32-lane swap pairs
+    // token 0's upper half with token 1's lower half), with one, of its two
+    // halves; the 16-lane swap then folds the remaining pair of groups; key
+    // scale and store
     auto epilogue = [&](const v4f (&C)[kLgTokensPerWave][kLgHeadBlocks], float ks, int rel) {
         float acc[kLgTokensPerWave];
 #pragma unroll
@@ -232,7 +251,7 @@ void mqa_logits_kernel(LogitsParams p) {
                     acc[i] = __builtin_fmaf(G[i][hb][e], relu(C[i][hb][e]), acc[i]);
         }
         const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]),
-                                                        __float_as_uint(acc[1]), false, false);
+                                                        __float_as_uint(acc[TPW - 1]), false, false);
         const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
         const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2),
                                                         false, false);
@@ -245,6 +264,15 @@ void mqa_logits_kernel(LogitsParams p) {
     fetch(key0, slot_cur);
     slots_at(key0 + kLgStage, slot_next);
     int buf = 0;
+    // One token per wavefront: each block's MFMAs are issued before the
+    // previous block's epilogue (its results held over in Cp), so the matrix
+    // unit works on one block while the VALU finishes the other, across the
+    // stage barriers too.  Two tokens run each block's MFMAs and epilogue in
+    // turn (their registers leave no room for a second set of results).
+    v4f Cp[kLgTokensPerWave][kLgHeadBlocks];
+    float ksp = 0.f;
+    int relp = 0;
+    bool havep = false;
 #pragma unroll 1
     for (int r0 = 0; r0 < nkeys; r0 += kLgStage, buf ^= 1) {
         stash(buf);
@@ -255,10 +283,15 @@ void mqa_logits_kernel(LogitsParams p) {
         }
         // each block's key operand and scale are read from LDS one block ahead,
         // so their latency hides behind the epilogue of the block before
+        constexpr bool kAhead = LgShape<TPW>::kReadAhead;
         v8i Bn = load32(&kbuf[buf][(lane & 15) * kLgRowPitch + 32 * g]);
         float ksn = kscl[buf][lane & 15];
 #pragma unroll
         for (int kb = 0; kb < kLgStage / 16; ++kb) {
+            if (!kAhead && kb > 0) {
+                Bn = load32(&kbuf[buf][(kb * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
+                ksn = kscl[buf][kb * 16 + (lane & 15)];
+            }
             const v8i B = Bn;
             const float ks = ksn;
             const int rel = r0 + kb * 16 + (lane & 15);
@@ -269,13 +302,23 @@ void mqa_logits_kernel(LogitsParams p) {
             for (int i = 0; i < kLgTokensPerWave; ++i)
 #pragma unroll
                 for (int hb = 0; hb < kLgHeadBlocks; ++hb) C[i][hb] = dots16(A[i][hb], B);
-            if (kb + 1 < kLgStage / 16) {
+            if (kAhead && kb + 1 < kLgStage / 16) {
                 Bn = load32(&kbuf[buf][((kb + 1) * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
                 ksn = kscl[buf][(kb + 1) * 16 + (lane & 15)];
             }
-            epilogue(C, ks, rel);
+            if (TPW == 2) {
+                epilogue(C, ks, rel);
+            } else {
+                if (kb > 0 || havep) epilogue(Cp, ksp, relp);
+#pragma unroll
+                for (int hb = 0; hb < kLgHeadBlocks; ++hb) Cp[0][hb] = C[0][hb];
+                ksp = ks;
+                relp = rel;
+            }
         }
+        havep = true;
     }
+    if (TPW == 1 && havep) epilogue(Cp, ksp, relp);
 }
 
 }  // namespace
@@ -284,8 +327,11 @@ hipError_t launch_logits(const LogitsParams& p, hipStream_t stream) {
     LogitsParams a = p;
     const int64_t tb = (p.T + kLogitsTokensPerBlock - 1) / kLogitsTokensPerBlock;
     void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&mqa_logits_kernel),
-                           dim3((unsigned)(tb * p.chunks)), dim3(kLgThreads), args, 0, stream);
+    if (p.tokens_per_wave == 1)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&mqa_logits_kernel<1>),
+                               dim3((unsigned)(tb * p.chunks)), dim3(LgShape<1>::kThreads), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&mqa_logits_kernel<2>),
+                           dim3((unsigned)(tb * p.chunks)), dim3(LgShape<2>::kThreads), args, 0, stream);
 }
 
 }  // namespace dsaidx
