@@ -24,10 +24,17 @@
 //     double-buffered, one barrier per stage; its rows are 144 bytes apart so
 //     that the 16 lanes of a B-operand read hit distinct banks;
 //   - each wavefront issues 2 x 12 MFMAs per 32 elements, accumulating in
-//     fp32.
-// The next stage's loads are issued before the current stage's MFMAs.  The
-// call is bound by the hidden states' HBM traffic: the weight (0.3 % of the
-// bytes at d = 7168) is re-read from L2 by every workgroup.
+//     fp32, with each weight operand read from LDS a few operands ahead
+//     (the order is pinned with scheduling groups: the compiler otherwise
+//     reads each operand just before its MFMAs).
+// Each stage first issues the next stage's weight slice and hidden rows; the
+// stage ends with an LDS-only wait and a bare barrier, so the hidden rows stay
+// in flight across it.  The weight (0.3 % of the bytes at d = 7168) is re-read
+// from L2 by every workgroup.  The hidden rows have one stage to arrive:
+// loads retire in issue order, so the wait for the next weight slice at the
+// end of a stage is also a wait for the rows issued before it.  Two stages
+// would need a second set of weight registers, which the 256 registers per
+// wavefront at two wavefronts per SIMD do not leave.
 #include "dsaidx_prep_device.h"
 
 #pragma clang fp contract(off)
@@ -61,6 +68,20 @@ __device__ __forceinline__ uint4 load16_keep(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+typedef uint4 ARows[2][2];   // a wavefront's hidden-row operands of one stage: [row block][k half]
+
+#ifndef DSAIDX_PROJ_AHEAD_B
+#define DSAIDX_PROJ_AHEAD_B 4
+#endif
+constexpr int kAheadB = DSAIDX_PROJ_AHEAD_B;   // weight operands read from LDS ahead of their MFMAs
+
+// Workgroup barrier after this wavefront's LDS writes have completed, with
+// its global loads left in flight (a full __syncthreads() also waits for
+// those).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int STYLE, int LAYOUT>
 __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a) {
     __shared__ __align__(16) uint8_t smem[2 * kWStageBytes];
@@ -76,13 +97,21 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
 
     for (int64_t blk = blockIdx.x; blk < a.row_blocks; blk += gridDim.x) {
         const int64_t row0 = blk * kProjRows;
+        // Operand rows, clamped: a token past T reads row T - 1 and a column
+        // past 128 + H reads the last weight row (their results are never
+        // stored), so every load below is unconditional and the compiler's
+        // waits stay exact.
         const uint16_t* arow[2];
-        bool aval[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int64_t t = row0 + 32 * wave + 16 * i + lr;
-            aval[i] = t < T;
-            arow[i] = a.x + (aval[i] ? t : 0) * a.x_st + 8 * lq;
+            arow[i] = a.x + (t < T ? t : T - 1) * a.x_st + 8 * lq;
+        }
+        const uint16_t* wrow[6];
+#pragma unroll
+        for (int jj = 0; jj < 6; ++jj) {
+            const int n = wr0 + 32 * jj;
+            wrow[jj] = a.w + (int64_t)(n < a.n_out ? n : a.n_out - 1) * a.w_st + 8 * wc;
         }
         f32x4 acc[2][kColBlocks];
 #pragma unroll
@@ -90,57 +119,84 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
 #pragma unroll
             for (int cb = 0; cb < kColBlocks; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        uint4 wreg[6], areg[2][2];
-        auto load_stage = [&](int s, uint4 (&w)[6], uint4 (&x)[2][2]) {
+        auto fetch_a = [&](int s, ARows& x) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    x[i][ks] = aval[i] ? load16(arow[i] + s * kStageK + 32 * ks) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int jj = 0; jj < 6; ++jj) {
-                const int n = wr0 + 32 * jj;
-                w[jj] = n < a.n_out ? load16_keep(a.w + (int64_t)n * a.w_st + s * kStageK + 8 * wc)
-                                    : make_uint4(0, 0, 0, 0);
-            }
+                for (int ks = 0; ks < 2; ++ks) x[i][ks] = load16(arow[i] + s * kStageK + 32 * ks);
         };
-        auto store_stage = [&](int buf, const uint4 (&w)[6]) {
+        auto fetch_w = [&](int s, uint4 (&w)[6]) {
+#pragma unroll
+            for (int jj = 0; jj < 6; ++jj) w[jj] = load16_keep(wrow[jj] + s * kStageK);
+        };
+        auto store_w = [&](int buf, const uint4 (&w)[6]) {
             uint8_t* base = smem + buf * kWStageBytes + 16 * wc;
 #pragma unroll
             for (int jj = 0; jj < 6; ++jj)
                 *reinterpret_cast<uint4*>(base + (wr0 + 32 * jj) * kWPitch) = w[jj];
         };
-
-        load_stage(0, wreg, areg);
-        store_stage(0, wreg);
-        __syncthreads();
-        for (int s = 0; s < stages; ++s) {
-            uint4 wnext[6], anext[2][2];
-            const bool more = s + 1 < stages;
-            if (more) load_stage(s + 1, wnext, anext);
+        // Stage s: the weight slice and the hidden rows of stage s + 1 are
+        // issued (the weight first), the MFMAs of stage s run on `cur` and
+        // weight buffer s & 1, each weight operand read from LDS kAheadB
+        // operands before its MFMAs, and the next weight slice goes to the
+        // other buffer before the stage's one barrier.  The last stage
+        // re-fetches itself instead of branching.
+        auto stage = [&](int s, const ARows& cur, ARows& fut) {
+            uint4 wn[6];
+            const int nx = s + 1 < stages ? s + 1 : s;
+            fetch_w(nx, wn);
+            fetch_a(nx, fut);
             const uint8_t* wb = smem + (s & 1) * kWStageBytes + lr * kWPitch + 16 * lq;
+            auto bread = [&](int o) -> uint4 {       // operand o = 12 ks + cb
+                return *reinterpret_cast<const uint4*>(wb + (o % kColBlocks) * 16 * kWPitch +
+                                                       64 * (o / kColBlocks));
+            };
+            constexpr int kOps = 2 * kColBlocks;
+            uint4 bq[kAheadB];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 a0 = __builtin_bit_cast(bf16x8, areg[0][ks]);
-                const bf16x8 a1 = __builtin_bit_cast(bf16x8, areg[1][ks]);
+            for (int o = 0; o < kAheadB; ++o) bq[o] = bread(o);
 #pragma unroll
-                for (int cb = 0; cb < kColBlocks; ++cb) {
-                    const bf16x8 b = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const uint4*>(wb + cb * 16 * kWPitch + 64 * ks));
-                    acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][cb], 0, 0, 0);
-                    acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][cb], 0, 0, 0);
-                }
+            for (int o = 0; o < kOps; ++o) {
+                const int ks = o / kColBlocks, cb = o % kColBlocks;
+                const bf16x8 b = __builtin_bit_cast(bf16x8, bq[o % kAheadB]);
+                if (o + kAheadB < kOps) bq[o % kAheadB] = bread(o + kAheadB);
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, cur[0][ks]);
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, cur[1][ks]);
+                acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][cb], 0, 0, 0);
+                acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][cb], 0, 0, 0);
             }
-            if (more) {
-                store_stage((s + 1) & 1, wnext);
+            // the order above, kept by the scheduler: the stage's global loads,
+            // the first kAheadB weight reads, then two MFMAs per further read
+            __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kAheadB, 0);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    areg[i][0] = anext[i][0];
-                    areg[i][1] = anext[i][1];
-                }
+            for (int o = kAheadB; o < kOps; ++o) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __syncthreads();
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAheadB, 0);
+            store_w((s + 1) & 1, wn);
+            lds_barrier();
+        };
+
+        ARows A0, A1;
+        {
+            uint4 w0[6];
+            fetch_w(0, w0);
+            fetch_a(0, A0);
+            store_w(0, w0);
         }
+        __syncthreads();
+        // two stages per iteration alternate the operand sets; an odd last
+        // stage runs after the loop, so that its body has no branches (they
+        // would make the compiler's waits conservative)
+        int s = 0;
+        for (; s + 2 <= stages; s += 2) {
+            stage(s, A0, A1);
+            stage(s + 1, A1, A0);
+        }
+        if (s < stages) stage(s, A0, A1);
+        __syncthreads();
 
         // Epilogue 1: the projection's output rounded to bf16 (nearest even),
         // staged in LDS (the stage buffers are free): key rows [128][128] and
