@@ -328,7 +328,8 @@ dsaidx_status dsaidx_proj_k_norm_rope_quant_store(const dsaidx_proj_args* j, con
     p.k_out = j->k_out;
     p.ko_st = j->k_out_stride_t;
     p.row_blocks = ceil_div(k->num_tokens, dsaidx::kProjRows);
-    const int64_t grid = p.row_blocks < max_grid(256) ? p.row_blocks : max_grid(256);
+    const int64_t grid = p.row_blocks < max_grid(dsaidx::kProjThreads) ? p.row_blocks
+                                                                      : max_grid(dsaidx::kProjThreads);
     return to_status(dsaidx::launch_proj(p, rope->style, (unsigned)grid,
                                          reinterpret_cast<hipStream_t>(stream)));
 }

@@ -201,6 +201,8 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
     key_row<STYLE, LAYOUT>(p, valid, raw, pos, slot, lane);
 }
 
+static_assert(256 / 64 <= kXchgWaves, "rope_generic's exchange buffer covers every wavefront");
+
 template <int STYLE, int LAYOUT, int HPI, bool KF>
 __global__ __launch_bounds__(256) void indexer_qk_prep_kernel(PrepParams p) {
     const int lane = threadIdx.x & 63;

@@ -336,9 +336,13 @@ __device__ __forceinline__ void rotate_neox(float x[8], const float xp[8], const
 // wavefront's own slots are touched, and a wavefront's LDS accesses complete
 // in issue order, so no workgroup barrier is involved: the wave barriers only
 // keep the compiler from moving the accesses across each other.
+// Wavefronts per workgroup the exchange buffer of rope_generic serves (every
+// kernel that reaches it asserts that its workgroups are no larger).
+constexpr int kXchgWaves = 4;
+
 template <int STYLE>
 __device__ __forceinline__ void rope_generic(float x[8], const RopeLane& rl) {
-    __shared__ __align__(16) float xchg[256 / 64][kRowsPerWave][kRow];
+    __shared__ __align__(16) float xchg[kXchgWaves][kRowsPerWave][kRow];
     const int lane = threadIdx.x & 63;
     const int j = lane & (kLanesPerRow - 1);
     float* row = xchg[threadIdx.x >> 6][lane >> 4];

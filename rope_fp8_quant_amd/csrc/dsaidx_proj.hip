@@ -45,7 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kProjThreads;
 constexpr int kColBlocks = kProjMaxCols / 16;        // 12 blocks of 16 output columns
 constexpr int kStageK = 64;                          // hidden elements per stage
 constexpr int kWPitch = kStageK * 2 + 16;            // LDS bytes per weight row (144)
@@ -54,6 +54,7 @@ constexpr int kKPitch = kRow * 2 + 16;               // LDS bytes per staged key
 constexpr int kGPitch = kProjMaxHeads * 2 + 16;      // LDS bytes per staged gate row (144)
 static_assert(kProjRows * (kKPitch + kGPitch) <= 2 * kWStageBytes, "epilogue staging fits the stages");
 static_assert(kProjRows == 32 * (kThreads / 64), "32 tokens per wavefront");
+static_assert(kThreads / 64 <= kXchgWaves, "rope_generic's exchange buffer covers every wavefront");
 
 // The lane's eight bf16 values of one staged key row (layout order), from LDS.
 template <int LAYOUT>
