@@ -107,12 +107,38 @@ def check(got, q8, w, codes, scale, key_slots=None, lengths=None, N=None):
 @pytest.mark.parametrize("T,H,S", [(64, 64, 4096), (41, 64, 1000), (9, 16, 300), (3, 1, 70),
                                    (17, 33, 129), (8, 63, 64)])
 def test_dense_keys(T, H, S):
+    """One-token shape (grids of at most 512 workgroups)."""
+    assert logits_grid(T, S) <= 512
     rng = np.random.default_rng(T * 1000 + H + S)
     q8, w = random_query(T, H, rng)
     codes, scale = random_cache(S, rng)
     got = run(q8, w, codes, scale)
     r = check(got, q8, w, codes, scale)
     print("\n[parity] logits T=%d H=%d N=%d max err / bound %.3g" % (T, H, S, r), flush=True)
+
+
+def logits_grid(T, N):
+    """Workgroups of a logits call (the host's chunking: about 3072 workgroups
+    of 8 tokens, at least 256 keys each); above 512 the kernel runs two
+    tokens per wavefront, at or below one."""
+    blocks = -(-T // 8)
+    want = max(1, min(-(-3072 // blocks), -(-N // 256)))
+    chunk = -(-(-(-N // want)) // 128) * 128
+    return blocks * -(-N // chunk)
+
+
+@pytest.mark.parametrize("T,H,S,causal", [(2045, 64, 600, False), (1603, 24, 900, True)])
+def test_two_tokens_per_wavefront_shape(T, H, S, causal):
+    """Calls large enough for the two-token shape, checked in full: a ragged
+    token count, heads not a multiple of 16, causal lengths."""
+    assert logits_grid(T, S) > 512
+    rng = np.random.default_rng(T + H)
+    q8, w = random_query(T, H, rng)
+    codes, scale = random_cache(S, rng)
+    lengths = np.clip(np.arange(T) * S // T + 1, 0, S) if causal else None
+    got = run(q8, w, codes, scale, lengths=lengths, stride_pad=3)
+    r = check(got, q8, w, codes, scale, lengths=lengths)
+    print("\n[parity] logits two-token shape T=%d H=%d N=%d max err / bound %.3g" % (T, H, S, r), flush=True)
 
 
 def test_causal_lengths_and_ragged_edges():
