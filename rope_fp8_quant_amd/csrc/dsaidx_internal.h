@@ -100,7 +100,7 @@ hipError_t launch_fp8_selftest(const float* in, uint8_t* out, int64_t n, float s
 // (one dispatch): out = hidden [T, d] x W[128 + H, d]^T in fp32 on the matrix
 // cores, rounded to bf16; columns 0..127 go through the key preparation of
 // `prep` (its k / k_st are unused), columns 128.. are written to gates.
-constexpr int kProjRows = 128;       // tokens per workgroup
+constexpr int kProjRows = 256;       // tokens per workgroup
 constexpr int kProjThreads = 256;    // 4 wavefronts per workgroup
 constexpr int kProjMaxHeads = 64;    // gate columns at most
 constexpr int kProjMaxCols = kRow + kProjMaxHeads;

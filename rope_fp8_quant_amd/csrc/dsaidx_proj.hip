@@ -13,17 +13,20 @@
 // call.  The key values are rounded to bf16 first, as the GEMM's output is, so
 // the cache holds what the preparation would store from that output.
 //
-// Mapping.  A workgroup of four wavefronts owns 128 tokens and all 128 + H
-// (at most 192) output columns; wavefront w owns tokens 32w .. 32w + 31 as two
-// 16-row blocks.  The contraction runs in stages of 64 hidden elements with
-// v_mfma_f32_16x16x32_bf16 (A: 16 tokens x 32, B: 32 x 16 columns):
+// Mapping.  A workgroup of four wavefronts owns 256 tokens and all 128 + H
+// (at most 192) output columns; wavefront w owns tokens 64w .. 64w + 63 as four
+// 16-row blocks, with its 4 x 12 accumulator blocks in AGPRs (one wavefront
+// per SIMD: 512 registers; 64 rows per wavefront halve the weight operand
+// reads from LDS per token against 32).  The contraction runs in stages of
+// 64 hidden elements with v_mfma_f32_16x16x32_bf16 (A: 16 tokens x 32, B:
+// 32 x 16 columns):
 //   - hidden rows go straight from HBM into the A operands (16 bytes per lane,
 //     lane l: token l % 16, elements 8 (l / 16) ..), nontemporal: every
 //     element is read once;
 //   - the stage's weight slice (192 rows x 128 bytes) goes through LDS,
 //     double-buffered, one barrier per stage; its rows are 144 bytes apart so
 //     that the 16 lanes of a B-operand read hit distinct banks;
-//   - each wavefront issues 2 x 12 MFMAs per 32 elements, accumulating in
+//   - each wavefront issues 4 x 12 MFMAs per 32 elements, accumulating in
 //     fp32, with each weight operand read from LDS a few operands ahead
 //     (the order is pinned with scheduling groups: the compiler otherwise
 //     reads each operand just before its MFMAs).
@@ -33,8 +36,8 @@
 // from L2 by every workgroup.  The hidden rows have one stage to arrive:
 // loads retire in issue order, so the wait for the next weight slice at the
 // end of a stage is also a wait for the rows issued before it.  Two stages
-// would need a second set of weight registers, which the 256 registers per
-// wavefront at two wavefronts per SIMD do not leave.
+// would need a second set of weight registers and of hidden rows, which the
+// 512 registers of one wavefront per SIMD do not leave.
 #include "dsaidx_prep_device.h"
 
 #pragma clang fp contract(off)
@@ -52,8 +55,8 @@ constexpr int kWPitch = kStageK * 2 + 16;            // LDS bytes per weight row
 constexpr int kWStageBytes = kProjMaxCols * kWPitch;   // 27648
 constexpr int kKPitch = kRow * 2 + 16;               // LDS bytes per staged key row (272)
 constexpr int kGPitch = kProjMaxHeads * 2 + 16;      // LDS bytes per staged gate row (144)
-static_assert(kProjRows * (kKPitch + kGPitch) <= 2 * kWStageBytes, "epilogue staging fits the stages");
-static_assert(kProjRows == 32 * (kThreads / 64), "32 tokens per wavefront");
+constexpr int kSmemBytes = kProjRows * (kKPitch + kGPitch) > 2 * kWStageBytes ? kProjRows * (kKPitch + kGPitch) : 2 * kWStageBytes;
+static_assert(kProjRows == 64 * (kThreads / 64), "64 tokens per wavefront");
 static_assert(kThreads / 64 <= kXchgWaves, "rope_generic's exchange buffer covers every wavefront");
 
 // The lane's eight bf16 values of one staged key row (layout order), from LDS.
@@ -69,7 +72,7 @@ __device__ __forceinline__ uint4 load16_keep(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
-typedef uint4 ARows[2][2];   // a wavefront's hidden-row operands of one stage: [row block][k half]
+typedef uint4 ARows[4][2];   // a wavefront's hidden-row operands of one stage: [row block][k half]
 
 #ifndef DSAIDX_PROJ_AHEAD_B
 #define DSAIDX_PROJ_AHEAD_B 4
@@ -84,8 +87,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int STYLE, int LAYOUT>
-__global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a) {
-    __shared__ __align__(16) uint8_t smem[2 * kWStageBytes];
+__global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a) {
+    __shared__ __align__(16) uint8_t smem[kSmemBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,10 +105,10 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
         // past 128 + H reads the last weight row (their results are never
         // stored), so every load below is unconditional and the compiler's
         // waits stay exact.
-        const uint16_t* arow[2];
+        const uint16_t* arow[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t t = row0 + 32 * wave + 16 * i + lr;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = row0 + 64 * wave + 16 * i + lr;
             arow[i] = a.x + (t < T ? t : T - 1) * a.x_st + 8 * lq;
         }
         const uint16_t* wrow[6];
@@ -114,15 +117,15 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
             const int n = wr0 + 32 * jj;
             wrow[jj] = a.w + (int64_t)(n < a.n_out ? n : a.n_out - 1) * a.w_st + 8 * wc;
         }
-        f32x4 acc[2][kColBlocks];
+        f32x4 acc[4][kColBlocks];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int cb = 0; cb < kColBlocks; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         auto fetch_a = [&](int s, ARows& x) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) x[i][ks] = load16(arow[i] + s * kStageK + 32 * ks);
         };
@@ -161,21 +164,21 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
                 const int ks = o / kColBlocks, cb = o % kColBlocks;
                 const bf16x8 b = __builtin_bit_cast(bf16x8, bq[o % kAheadB]);
                 if (o + kAheadB < kOps) bq[o % kAheadB] = bread(o + kAheadB);
-                const bf16x8 a0 = __builtin_bit_cast(bf16x8, cur[0][ks]);
-                const bf16x8 a1 = __builtin_bit_cast(bf16x8, cur[1][ks]);
-                acc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][cb], 0, 0, 0);
-                acc[1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][cb], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur[i][ks]), b,
+                                                                          acc[i][cb], 0, 0, 0);
             }
             // the order above, kept by the scheduler: the stage's global loads,
             // the first kAheadB weight reads, then two MFMAs per further read
-            __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 14, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, kAheadB, 0);
 #pragma unroll
             for (int o = kAheadB; o < kOps; ++o) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAheadB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * kAheadB, 0);
             store_w((s + 1) & 1, wn);
             lds_barrier();
         };
@@ -206,12 +209,12 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
         uint8_t* ktile = smem;
         uint8_t* gtile = smem + kProjRows * kKPitch;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int cb = 0; cb < kColBlocks; ++cb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 32 * wave + 16 * i + 4 * lq + e;
+                    const int r = 64 * wave + 16 * i + 4 * lq + e;
                     const int c = 16 * cb + lr;
                     const uint16_t v = (uint16_t)(__float_as_uint(round_bf16(acc[i][cb][e])) >> 16);
                     if (c < kRow)
@@ -241,8 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void proj_key_prep_kernel(ProjParams a
         // preparation's key-row code (LayerNorm, RoPE, quantisation, store).
         const int g = lane >> 4;
         const int j = lane & (kLanesPerRow - 1);
-        for (int pass = 0; pass < 8; ++pass) {
-            const int r = 32 * wave + 4 * pass + g;
+        for (int pass = 0; pass < 16; ++pass) {
+            const int r = 64 * wave + 4 * pass + g;
             const int64_t t = row0 + r;
             const bool valid = t < T;
             const uint4 raw = lds_row<LAYOUT>(ktile + r * kKPitch, j);

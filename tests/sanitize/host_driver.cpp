@@ -657,7 +657,7 @@ void logits_calls() {
     });
 }
 
-// The projection entry: one dispatch of ceil(T / 128) workgroups, the key
+// The projection entry: one dispatch of ceil(T / kProjRows) workgroups, the key
 // side filled as for the key entry (its row pointer unused), every rejected
 // argument enqueuing nothing.
 void projection_calls() {
@@ -684,7 +684,8 @@ void projection_calls() {
     CHECK(g_launches.size() == 1 && g_launches[0].kind == 5);
     if (!g_launches.empty()) {
         const Launch& l = g_launches[0];
-        CHECK(l.grid == 3 && l.rows == 3 && l.n == 7168 && l.k == 64 && l.style == 0);
+        const int64_t blocks = (300 + dsaidx::kProjRows - 1) / dsaidx::kProjRows;
+        CHECK(l.grid == blocks && l.rows == blocks && l.n == 7168 && l.k == 64 && l.style == 0);
         CHECK(l.p.T == 300 && l.p.k == nullptr && l.p.loc == k.out_cache_loc && l.p.S == k.num_slots);
         CHECK(l.workspace == nullptr);
     }
