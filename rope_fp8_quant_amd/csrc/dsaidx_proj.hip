@@ -50,12 +50,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = kProjThreads;
 constexpr int kColBlocks = kProjMaxCols / 16;        // 12 blocks of 16 output columns
-constexpr int kStageK = 64;                          // hidden elements per stage
+constexpr int kStageK = kProjStageK;                 // hidden elements per stage (64)
 constexpr int kWPitch = kStageK * 2 + 16;            // LDS bytes per weight row (144)
 constexpr int kWStageBytes = kProjMaxCols * kWPitch;   // 27648
 constexpr int kKPitch = kRow * 2 + 16;               // LDS bytes per staged key row (272)
 constexpr int kGPitch = kProjMaxHeads * 2 + 16;      // LDS bytes per staged gate row (144)
-constexpr int kSmemBytes = kProjRows * (kKPitch + kGPitch) > 2 * kWStageBytes ? kProjRows * (kKPitch + kGPitch) : 2 * kWStageBytes;
+// LDS: the two weight stages during the contraction, then the epilogue's
+// staging of the block's key and gate rows (106496 bytes at 256 tokens).
+constexpr int kEpilogueBytes = kProjRows * (kKPitch + kGPitch);
+constexpr int kSmemBytes = kEpilogueBytes > 2 * kWStageBytes ? kEpilogueBytes : 2 * kWStageBytes;
 static_assert(kProjRows == 64 * (kThreads / 64), "64 tokens per wavefront");
 static_assert(kThreads / 64 <= kXchgWaves, "rope_generic's exchange buffer covers every wavefront");
 
@@ -86,6 +89,8 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One wavefront per SIMD: each holds 192 accumulators (in AGPRs) and its
+// operands in the 512 registers that leaves.
 template <int STYLE, int LAYOUT>
 __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a) {
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
@@ -170,7 +175,8 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
                                                                           acc[i][cb], 0, 0, 0);
             }
             // the order above, kept by the scheduler: the stage's global loads,
-            // the first kAheadB weight reads, then two MFMAs per further read
+            // the first kAheadB weight reads, then the four MFMAs of each
+            // operand with the next operand's read
             __builtin_amdgcn_sched_group_barrier(0x020, 14, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, kAheadB, 0);
 #pragma unroll
@@ -203,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
         __syncthreads();
 
         // Epilogue 1: the projection's output rounded to bf16 (nearest even),
-        // staged in LDS (the stage buffers are free): key rows [128][128] and
-        // gate rows [128][H].  Lane l holds column l % 16 of rows 4 (l / 16) ..
+        // staged in LDS (the stage buffers are free): key rows [256][128] and
+        // gate rows [256][H].  Lane l holds column l % 16 of rows 4 (l / 16) ..
         // + 3 of each 16 x 16 block.
         uint8_t* ktile = smem;
         uint8_t* gtile = smem + kProjRows * kKPitch;
