@@ -356,15 +356,16 @@ int64_t dsaidx_topk_workspace_bytes(int64_t rows, int64_t cols, int32_t k);
  * 128-term sums and the head sum are fp32, in an order the library chooses.
  *   q_fp8          E4M3FN codes [T, H, 128], contiguous (the prep call's q_fp8), 16-byte aligned
  *   weights        fp32 [T, H], contiguous (the prep call's weights_out), 4-byte aligned
- *   num_tokens     T >= 0
+ *   num_tokens     T in [0, 2^31)
  *   num_heads      H in [1, 64]
  *   flags          0, or DSAIDX_K_PAGED_CACHE for the page-interleaved layout
  *   k_cache, k_cache_row_stride, k_scale, num_slots, page_size
  *                  the index-K cache, read only, as in dsaidx_k_args
  *   key_slots      int32 [num_keys]: the cache slot of each key (a page table's
  *                  flattening), 4-byte aligned; NULL: key s is slot s, and then
- *                  num_keys <= num_slots.  A slot outside [0, num_slots) reads
- *                  no memory and its logit is 0
+ *                  num_keys <= num_slots.  A slot outside [0, num_slots) is
+ *                  never addressed (slot 0's row is read in its place and
+ *                  discarded) and its logit is 0
  *   num_keys       N in [0, 2^31)
  *   lengths        int32 [T], 4-byte aligned: query t scores keys
  *                  [0, min(max(lengths[t], 0), N)); NULL: all N

@@ -402,7 +402,8 @@ static void page_divisor(int64_t d, uint32_t* magic, int32_t* shift) {
 }
 
 dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t stream) {
-    if (!a || !token_count_ok(a->num_tokens) || a->num_keys < 0 || a->num_keys >= (int64_t(1) << 31))
+    if (!a || a->num_tokens < 0 || a->num_tokens >= (int64_t(1) << 31) || a->num_keys < 0 ||
+        a->num_keys >= (int64_t(1) << 31))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (a->num_tokens == 0 || a->num_keys == 0) return DSAIDX_OK;
     if (a->num_heads < 1 || a->num_heads > dsaidx::kLogitsMaxHeads) return DSAIDX_ERR_INVALID_ARGUMENT;
@@ -425,35 +426,42 @@ dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t str
     }
     if (!a->key_slots && a->num_keys > a->num_slots) return DSAIDX_ERR_INVALID_ARGUMENT;
     if (a->logits_stride < a->num_keys) return DSAIDX_ERR_INVALID_ARGUMENT;
+    const int64_t blocks = ceil_div(a->num_tokens, dsaidx::kLogitsTokensPerBlock);
+    int64_t chunks = 0;
+    const int64_t chunk = logits_key_chunk(a->num_tokens, a->num_keys, &chunks);
+    if (blocks * chunks >= (int64_t(1) << 31)) return DSAIDX_ERR_INVALID_ARGUMENT;
     dsaidx::LogitsParams p;
     std::memset(&p, 0, sizeof p);
     p.q = a->q_fp8;
     p.w = a->weights;
-    p.T = a->num_tokens;
+    p.T = (int32_t)a->num_tokens;
     p.H = a->num_heads;
     p.k_cache = a->k_cache;
     p.k_row_stride = paged ? 0 : a->k_cache_row_stride;
     p.k_scale = paged ? nullptr : a->k_scale;
-    p.S = a->num_slots;
-    p.page_size = paged ? a->page_size : 0;
+    p.S = (uint32_t)(a->num_slots < (int64_t(1) << 31) ? a->num_slots : (int64_t(1) << 31));
+    p.page_size = paged ? (int32_t)a->page_size : 0;
     if (paged) page_divisor(a->page_size, &p.page_magic, &p.page_shift);
     p.key_slots = a->key_slots;
-    p.N = a->num_keys;
+    p.N = (int32_t)a->num_keys;
     p.lengths = a->lengths;
     p.out = a->logits;
     p.out_stride = a->logits_stride;
-    p.chunk = logits_key_chunk(p.T, p.N, &p.chunks);
-    p.chunk_major = ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) >= p.chunks ? 1 : 0;
-    p.w_vec = (p.H % 4 == 0 && aligned(a->weights, 16)) ? 1 : 0;
+    p.chunk = (int32_t)chunk;
+    p.chunks = (int32_t)chunks;
+    p.blocks = (int32_t)blocks;
+    p.chunk_major = blocks >= chunks ? 1 : 0;
+    // the kernel splits its workgroup index by the magic-number division
+    // (Granlund-Montgomery, as for the page size): by the token blocks in
+    // chunk-major order, by the chunks in token-block-major order
+    page_divisor(p.chunk_major ? blocks : chunks, &p.grid_magic, &p.grid_shift);
     // One token per wavefront when the grid is one resident round (two of its
     // 8-wavefront workgroups per CU): its four wavefronts per SIMD and
     // pipelined blocks shorten a decode call (14.3-14.7 against 15.1-15.5 us
     // for 64 tokens x 16384 keys); larger calls keep two tokens per
     // wavefront, which reads each key operand for twice the MFMAs (285-293
     // against 275-281 us on the causal 8192-token prefill).
-    p.tokens_per_wave = ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) * p.chunks <= kLogitsOneRound ? 1 : 2;
-    if (ceil_div(p.T, dsaidx::kLogitsTokensPerBlock) * p.chunks >= (int64_t(1) << 31))
-        return DSAIDX_ERR_INVALID_ARGUMENT;
+    p.tokens_per_wave = blocks * chunks <= kLogitsOneRound ? 1 : 2;
     return to_status(dsaidx::launch_logits(p, reinterpret_cast<hipStream_t>(stream)));
 }
 

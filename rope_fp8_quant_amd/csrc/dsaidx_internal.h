@@ -138,24 +138,26 @@ constexpr int kLogitsStageKeys = 128;       // keys per LDS stage; chunks are mu
 struct LogitsParams {
     const uint8_t* q;          // [T, H, 128] E4M3 codes
     const float* w;            // [T, H] folded gates
-    int64_t T;
+    int32_t T;                 // query tokens, below 2^31
     int32_t H;
     const uint8_t* k_cache;
     int64_t k_row_stride;      // planar: bytes per slot row
     const float* k_scale;      // planar
-    int64_t S;                 // slots
-    int64_t page_size;         // page-interleaved layout: slots per page (0 = planar)
+    uint32_t S;                // slots, capped at 2^31 (every non-negative int32 slot below it is valid)
+    int32_t page_size;         // page-interleaved layout: slots per page (0 = planar)
     uint32_t page_magic;       // slot / page_size = (slot * page_magic) >> page_shift
     int32_t page_shift;        //   for every slot below 2^31
     const int32_t* key_slots;  // [N] or null (key s = slot s)
-    int64_t N;
+    int32_t N;                 // keys, below 2^31
     const int32_t* lengths;    // [T] or null
     float* out;
     int64_t out_stride;
-    int64_t chunk;             // keys per workgroup
-    int64_t chunks;            // key chunks: the grid is ceil(T / 8) * chunks
+    int32_t chunk;             // keys per workgroup (at most 2^30)
+    int32_t chunks;            // key chunks
+    int32_t blocks;            // token blocks, ceil(T / 8): the grid is blocks * chunks (below 2^31)
+    uint32_t grid_magic;       // workgroup / (chunk_major ? blocks : chunks) = (wg * grid_magic) >> grid_shift
+    int32_t grid_shift;
     int32_t chunk_major;       // workgroup order: chunk-major (1) or token-block-major (0)
-    int32_t w_vec;             // H % 4 == 0 and weights 16-byte aligned: gates read 4 at a time
     int32_t tokens_per_wave;   // 1: 8-wavefront workgroups, pipelined blocks; 2: 4 wavefronts
 };
 

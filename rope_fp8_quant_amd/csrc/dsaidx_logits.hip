@@ -37,6 +37,7 @@ namespace dsaidx {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kLgStage = kLogitsStageKeys;        // keys per LDS stage
@@ -82,14 +83,19 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
     return r;
 }
 
-__device__ __forceinline__ int64_t clamp_len(const LogitsParams& p, int64_t t) {
-    if (t >= p.T) return 0;
-    if (!p.lengths) return p.N;
-    const int64_t l = p.lengths[t];
-    return l < 0 ? 0 : (l < p.N ? l : p.N);
+// All-ones when ok, else zero: masks a value loaded from a clamped address,
+// so that no load sits under a per-lane branch.  (Under a divergent branch the
+// compiler must wait for the load before the other side writes the same
+// register, which serialises the loads of the set-up.)
+__device__ __forceinline__ int lane_mask(bool ok) { return ok ? -1 : 0; }
+__device__ __forceinline__ float masked(float v, int m) {
+    return __int_as_float(__float_as_int(v) & m);
 }
 
-template <int TPW>
+// SLOTS: the keys come from a slot list (else key s is slot s); a template
+// parameter rather than a branch, which would make the set-up wait for the
+// list's first entries inside it.
+template <int TPW, bool SLOTS>
 __global__ __launch_bounds__(LgShape<TPW>::kThreads)
 __attribute__((amdgpu_waves_per_eu(LgShape<TPW>::kMinWaves)))
 void mqa_logits_kernel(LogitsParams p) {
@@ -100,124 +106,172 @@ void mqa_logits_kernel(LogitsParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;                      // lane group: bytes [32 g, 32 g + 32)
+    // Index arithmetic is 32-bit (the host bounds T, N, the grid and the chunk
+    // below 2^31) and every wavefront repeats it, so it is kept short: the
+    // SIMD's four wavefronts share one scalar issue slot, and a long set-up
+    // holds back the second workgroup on the compute unit.
+    //
     // token blocks from the last: under causal lengths the longest rows go
-    // first, so the short ones fill in behind them instead of trailing
-    const int64_t nb = (p.T + TPB - 1) / TPB;
+    // first, so the short ones fill in behind them instead of trailing.
     // The 8 XCDs take consecutive workgroups in turn.  Chunk-major order
     // (consecutive workgroups: neighbouring token blocks of one chunk) gives
     // every XCD its share of every chunk whatever the chunk count, which
     // matters when chunks carry unequal work (causal lengths); token-major
     // order (consecutive workgroups: the chunks of one token block) keeps each
     // chunk's keys on one XCD when there are few token blocks and many chunks.
-    int64_t tb, key0;
+    const uint32_t bx = blockIdx.x;
+    const uint32_t qd = (uint32_t)(((uint64_t)bx * p.grid_magic) >> p.grid_shift);
+    int tb, key0;
     if (p.chunk_major) {
-        const int64_t ci = blockIdx.x / nb;
-        tb = nb - 1 - (blockIdx.x - ci * nb);
-        key0 = ci * p.chunk;
+        tb = p.blocks - 1 - (int)(bx - qd * (uint32_t)p.blocks);
+        key0 = (int)qd * p.chunk;
     } else {
-        const int64_t bi = blockIdx.x / p.chunks;
-        tb = nb - 1 - bi;
-        key0 = (blockIdx.x - bi * p.chunks) * p.chunk;
+        tb = p.blocks - 1 - (int)qd;
+        key0 = (int)(bx - qd * (uint32_t)p.chunks) * p.chunk;
     }
-    const int64_t t_first = tb * TPB;
+    const int t_first = tb * TPB;
 
+    constexpr int KPT = LgShape<TPW>::kKPT;
+    const int sk = tid >> 2, sp = tid & 3;
+    const int key1 = p.N - key0 < p.chunk ? p.N : key0 + p.chunk;
+
+    // Set-up loads.  Each reads a clamped, valid address (the host checks T,
+    // N, S >= 1 and 1 <= H <= 64) and is masked where it is used: a load
+    // whose result is changed under a branch, even a uniform one, makes the
+    // compiler wait for it inside the branch.  Loads retire in issue order, so
+    // they go out in the order they are needed: the block's lengths, the slot
+    // lists of the first two stages (the key rows depend on them), then the
+    // gates and query rows (first needed by the first MFMA).
+
+    // lane l reads the length of token t_first + l % 8
+    const int tl = t_first + (lane & (TPB - 1));
+    int32_t lraw = 0;
+    if (p.lengths) lraw = p.lengths[tl < p.T ? tl : p.T - 1];
+    // valid keys of token t_first + i (i wavefront-uniform)
+    auto length_of = [&](int i) -> int {
+        const int r = __builtin_amdgcn_readlane(lraw, i);
+        const int l = !p.lengths ? p.N : min(max(r, 0), p.N);
+        return t_first + i < p.T ? l : 0;
+    };
+    int kend = key1;      // lowered to the longest token's length below
     // keys past every token's length are skipped (the same for the workgroup)
-    int64_t kmax = 0;
+    auto chunk_end = [&]() {
+        int kmax = 0;
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) {
-        const int64_t l = clamp_len(p, t_first + i);
-        kmax = l > kmax ? l : kmax;
-    }
-    const int64_t key1 = key0 + p.chunk < p.N ? key0 + p.chunk : p.N;
-    const int64_t kend = key1 < kmax ? key1 : kmax;
-    if (kend <= key0) return;
+        for (int i = 0; i < TPB; ++i) kmax = max(kmax, length_of(i));
+        return min(key1, kmax);
+    };
+    // slot-list entries of the stage at s0, as read (slot_of drops the
+    // entries at or past kend when the rows are fetched, and ignores them
+    // without a slot list)
+    auto slots_at = [&](int s0, int32_t (&out)[KPT]) {
+        if constexpr (!SLOTS) return;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int s = s0 + 64 * j + sk;
+            out[j] = p.key_slots[min(s, p.N - 1)];
+        }
+    };
 
-    // this wavefront's tokens: q rows (A operands) and gates, zero past H or T
-    int64_t tok[kLgTokensPerWave], len[kLgTokensPerWave];
+    // Calls of one resident round (one token per wavefront) issue every load
+    // before the lengths arrive; larger calls first drop the workgroups with
+    // nothing to do (half of them under causal lengths) and load after.
+    constexpr bool kEarlyLoads = TPW == 1;
+    if constexpr (!kEarlyLoads) {
+        kend = chunk_end();
+        if (kend <= key0) return;
+    }
+    int32_t slot_cur[KPT], slot_next[KPT];
+    slots_at(key0, slot_cur);
+    slots_at(key0 + kLgStage, slot_next);
+    __builtin_amdgcn_sched_barrier(0);   // keep the slot loads ahead of the query rows
+
+    // this wavefront's tokens: gates (zero past H or T), then q rows (A
+    // operands).  A lane past H reads row H - 1 and one past T token T - 1:
+    // the first meets a zero gate (a finite dot times zero adds nothing, and a
+    // NaN code in that row already makes head H - 1's own dot NaN), the second
+    // writes nothing, so the rows need no mask (which would make the set-up
+    // wait for them before fetching the keys).
+    const int t_wave = t_first + wave * kLgTokensPerWave;
     v8i A[kLgTokensPerWave][kLgHeadBlocks];
     float G[kLgTokensPerWave][kLgHeadBlocks][4];
 #pragma unroll
     for (int i = 0; i < kLgTokensPerWave; ++i) {
-        const int64_t t = t_first + wave * kLgTokensPerWave + i;
-        tok[i] = t;
-        len[i] = clamp_len(p, t);
+        const int t = t_wave + i;
+        const float* wrow = p.w + (int64_t)min(t, p.T - 1) * p.H;
 #pragma unroll
-        for (int hb = 0; hb < kLgHeadBlocks; ++hb) {
-            const int h = hb * 16 + (lane & 15);
-            A[i][hb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            if (t < p.T && h < p.H) A[i][hb] = load32(p.q + ((t * p.H + h) * 128 + 32 * g));
-            if (p.w_vec) {
-                // the lane's four gates are adjacent: one 16-byte load
-                float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (t < p.T && hb * 16 + 4 * g < p.H)
-                    gv = *reinterpret_cast<const float4*>(p.w + t * p.H + hb * 16 + 4 * g);
-                G[i][hb][0] = gv.x; G[i][hb][1] = gv.y; G[i][hb][2] = gv.z; G[i][hb][3] = gv.w;
-            } else {
+        for (int hb = 0; hb < kLgHeadBlocks; ++hb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int hh = hb * 16 + 4 * g + e;
-                    G[i][hb][e] = (t < p.T && hh < p.H) ? p.w[t * p.H + hh] : 0.f;
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int hh = hb * 16 + 4 * g + e;
+                G[i][hb][e] = masked(wrow[min(hh, p.H - 1)], lane_mask(t < p.T && hh < p.H));
             }
-        }
+    }
+#pragma unroll
+    for (int i = 0; i < kLgTokensPerWave; ++i) {
+        const uint8_t* qrow = p.q + (int64_t)min(t_wave + i, p.T - 1) * p.H * 128 + 32 * g;
+#pragma unroll
+        for (int hb = 0; hb < kLgHeadBlocks; ++hb)
+            A[i][hb] = load32(qrow + min(hb * 16 + (lane & 15), p.H - 1) * 128);
+    }
+    if constexpr (kEarlyLoads) {
+        // The loads above stay above the exit: no memory access may move
+        // across this (empty) statement, so the compiler cannot sink them past
+        // the branch into the only path that uses them; and as it redefines
+        // the lengths register, their uses (and the wait for them) come after
+        // every load of the set-up has been issued.
+        asm volatile("" : "+v"(lraw) :: "memory");
+        kend = chunk_end();
+        if (kend <= key0) return;
     }
 
     // stage loader: thread tid brings keys tid / 4 + 64 j (j < KPT) of a
-    // stage, bytes [32 (tid % 4), +32) of each as four 8-byte loads, and the
-    // thread with tid % 4 = 0 their scales; a key past kend or with a slot
-    // outside the cache is all zeros.  The slot list is read one stage ahead
-    // into 32-bit registers and widened only when the rows are fetched, so
-    // the wavefront does not wait on it in the stage that loads it.
-    const int sk = tid >> 2, sp = tid & 3;
-    constexpr int KPT = LgShape<TPW>::kKPT;
-    auto slot_of = [&](int64_t s, int32_t raw) -> int64_t {
-        if (s >= kend) return -1;
-        return p.key_slots ? (int64_t)raw : s;
+    // stage, bytes [32 (tid % 4), +32) of each as four 8-byte loads, and its
+    // scale (stored by the thread with tid % 4 = 0); a key past kend or with a
+    // slot outside the cache reads slot 0 and is zeroed when stashed (masking
+    // at the fetch would make the wavefront wait for the rows there).  The
+    // slot list is read one stage ahead into 32-bit registers.
+    auto slot_ok = [&](int s, int32_t raw) {
+        return s < kend && (!SLOTS || (uint32_t)raw < p.S);
     };
     uint2 sreg[KPT][4];
     float sscale[KPT];
-    auto fetch = [&](int64_t s0, const int32_t (&raw)[KPT]) {
+    int smask[KPT];
+    auto fetch = [&](int s0, const int32_t (&raw)[KPT]) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const int64_t slot = slot_of(s0 + 64 * j + sk, raw[j]);
-            const bool ok = slot >= 0 && slot < p.S;
-            const uint8_t* row = nullptr;
-            const float* scl = nullptr;
-            if (ok) {
-                if (p.page_size) {
-                    const uint32_t pg = (uint32_t)(((uint64_t)slot * p.page_magic) >> p.page_shift);
-                    const int64_t o = slot - (int64_t)pg * p.page_size;
-                    const uint8_t* page = p.k_cache + (int64_t)pg * p.page_size * 132;
-                    row = page + o * 128;
-                    scl = reinterpret_cast<const float*>(page + p.page_size * 128) + o;
-                } else {
-                    row = p.k_cache + slot * p.k_row_stride;
-                    scl = p.k_scale + slot;
-                }
+            const int s = s0 + 64 * j + sk;
+            const bool ok = slot_ok(s, raw[j]);
+            const uint32_t sl = ok ? (SLOTS ? (uint32_t)raw[j] : (uint32_t)s) : 0u;
+            const uint8_t* row;
+            const float* scl;
+            if (p.page_size) {
+                const uint32_t pg = (uint32_t)(((uint64_t)sl * p.page_magic) >> p.page_shift);
+                const uint32_t o = sl - pg * (uint32_t)p.page_size;
+                const uint8_t* page = p.k_cache + (uint64_t)pg * ((uint32_t)p.page_size * 132u);
+                row = page + o * 128u;
+                scl = reinterpret_cast<const float*>(page + (uint32_t)p.page_size * 128u) + o;
+            } else {
+                row = p.k_cache + (uint64_t)sl * (uint64_t)p.k_row_stride;
+                scl = p.k_scale + sl;
             }
+            smask[j] = lane_mask(ok);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                sreg[j][m] = ok ? *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * m) : make_uint2(0u, 0u);
-            sscale[j] = 0.f;
-            if (sp == 0) sscale[j] = ok ? *scl : 0.f;
+            for (int q = 0; q < 4; ++q) sreg[j][q] = *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * q);
+            sscale[j] = *scl;
         }
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             uint8_t* d = &kbuf[buf][(sk + 64 * j) * kLgRowPitch + 32 * sp];
+            const uint32_t m = (uint32_t)smask[j];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) *reinterpret_cast<uint2*>(d + 8 * m) = sreg[j][m];
-            if (sp == 0) kscl[buf][sk + 64 * j] = sscale[j];
-        }
-    };
-    auto slots_at = [&](int64_t s0, int32_t (&out)[KPT]) {
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int64_t s = s0 + 64 * j + sk;
-            out[j] = (p.key_slots && s < kend) ? p.key_slots[s] : -1;
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2*>(d + 8 * q) = make_uint2(sreg[j][q].x & m, sreg[j][q].y & m);
+            if (sp == 0) kscl[buf][sk + 64 * j] = masked(sscale[j], smask[j]);
         }
     };
 
@@ -227,12 +281,12 @@ void mqa_logits_kernel(LogitsParams p) {
     // 32-bit)
     const int oi = TPW == 2 ? lane >> 5 : 0;
     const bool writer = TPW == 2 ? (lane & 16) == 0 : lane < 16;
-    const int64_t otok = oi ? tok[TPW - 1] : tok[0];
-    const int64_t olen = oi ? len[TPW - 1] : len[0];
-    const int64_t ostop = (olen < kend ? olen : kend) - key0;
-    const int lim = writer && ostop > 0 ? (int)ostop : 0;     // this lane stores keys rel < lim
-    float* const obase = p.out + (otok < p.T ? otok : 0) * p.out_stride + key0;
-    const int nkeys = (int)(kend - key0);
+    const int otok = t_wave + oi;
+    const int olen = oi ? length_of(wave * kLgTokensPerWave + TPW - 1) : length_of(wave * kLgTokensPerWave);
+    float* const obase = p.out + (int64_t)min(otok, p.T - 1) * p.out_stride + key0;
+    const int ostop = min(olen, kend) - key0;
+    const int lim = writer && ostop > 0 ? ostop : 0;     // this lane stores keys rel < lim
+    const int nkeys = kend - key0;
 
     // ReLU, gate and head sum of one block's dots, then the sum over the four
     // lane groups: with two tokens, for both at once (the 32-lane swap pairs
@@ -259,10 +313,7 @@ void mqa_logits_kernel(LogitsParams p) {
         if (rel < lim) obase[rel] = v * ks;
     };
 
-    int32_t slot_cur[KPT], slot_next[KPT];
-    slots_at(key0, slot_cur);
     fetch(key0, slot_cur);
-    slots_at(key0 + kLgStage, slot_next);
     int buf = 0;
     // One token per wavefront: each block's MFMAs are issued before the
     // previous block's epilogue (its results held over in Cp), so the matrix
@@ -325,13 +376,17 @@ void mqa_logits_kernel(LogitsParams p) {
 
 hipError_t launch_logits(const LogitsParams& p, hipStream_t stream) {
     LogitsParams a = p;
-    const int64_t tb = (p.T + kLogitsTokensPerBlock - 1) / kLogitsTokensPerBlock;
     void* args[] = {&a};
-    if (p.tokens_per_wave == 1)
-        return hipLaunchKernel(reinterpret_cast<const void*>(&mqa_logits_kernel<1>),
-                               dim3((unsigned)(tb * p.chunks)), dim3(LgShape<1>::kThreads), args, 0, stream);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&mqa_logits_kernel<2>),
-                           dim3((unsigned)(tb * p.chunks)), dim3(LgShape<2>::kThreads), args, 0, stream);
+    const dim3 grid((unsigned)p.blocks * (unsigned)p.chunks);
+    const bool slots = p.key_slots != nullptr;
+    if (p.tokens_per_wave == 1) {
+        const void* k = slots ? reinterpret_cast<const void*>(&mqa_logits_kernel<1, true>)
+                              : reinterpret_cast<const void*>(&mqa_logits_kernel<1, false>);
+        return hipLaunchKernel(k, grid, dim3(LgShape<1>::kThreads), args, 0, stream);
+    }
+    const void* k = slots ? reinterpret_cast<const void*>(&mqa_logits_kernel<2, true>)
+                          : reinterpret_cast<const void*>(&mqa_logits_kernel<2, false>);
+    return hipLaunchKernel(k, grid, dim3(LgShape<2>::kThreads), args, 0, stream);
 }
 
 }  // namespace dsaidx

@@ -599,6 +599,31 @@ void logits_calls() {
         CHECK(g_launches[2].lp.chunk == 128 && g_launches[2].lp.chunks == 1);
         CHECK(g_launches[2].lp.H == 3 && g_launches[2].lp.N == 100 && g_launches[2].lp.page_size == 0);
         CHECK(g_launches[2].lp.key_slots != nullptr && g_launches[2].lp.lengths != nullptr);
+        // the workgroup index splits by the magic-number division the kernel
+        // uses: checked for every workgroup of each grid
+        for (const auto& l : g_launches) {
+            const uint32_t d = l.lp.chunk_major ? (uint32_t)l.lp.blocks : (uint32_t)l.lp.chunks;
+            CHECK(l.lp.blocks == (l.lp.T + 7) / 8);
+            for (uint32_t b = 0; b < (uint32_t)l.lp.blocks * (uint32_t)l.lp.chunks; ++b)
+                CHECK((uint32_t)(((uint64_t)b * l.lp.grid_magic) >> l.lp.grid_shift) == b / d);
+        }
+    }
+    // the same division at the largest grid index and awkward divisors
+    {
+        g_launches.clear();
+        dsaidx_logits_args a = make((int64_t(1) << 31) - 8, 1, 1);   // 2^28 - 1 token blocks, one chunk
+        a.logits_stride = 1;
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        a = make(8 * 3, 64, (int64_t(1) << 31) - 1);                   // 3 token blocks, many chunks
+        a.num_slots = a.num_keys;
+        CHECK(dsaidx_mqa_logits(&a, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 2);
+        for (const auto& l : g_launches) {
+            const uint32_t d = l.lp.chunk_major ? (uint32_t)l.lp.blocks : (uint32_t)l.lp.chunks;
+            const uint32_t n = (uint32_t)l.lp.blocks * (uint32_t)l.lp.chunks;
+            for (uint32_t b : {0u, 1u, d - 1, d, d + 1, n / 2, n - 2, n - 1})
+                if (b < n) CHECK((uint32_t)(((uint64_t)b * l.lp.grid_magic) >> l.lp.grid_shift) == b / d);
+        }
     }
     // page-interleaved cache; empty calls
     {
@@ -625,6 +650,7 @@ void logits_calls() {
     };
     REJECT(dsaidx_mqa_logits(nullptr, nullptr));
     bad([](dsaidx_logits_args& a) { a.num_tokens = -1; });
+    bad([](dsaidx_logits_args& a) { a.num_tokens = int64_t(1) << 31; });
     bad([](dsaidx_logits_args& a) { a.num_keys = -1; });
     bad([](dsaidx_logits_args& a) { a.num_keys = int64_t(1) << 31; a.logits_stride = a.num_keys; });
     bad([](dsaidx_logits_args& a) { a.num_heads = 0; });

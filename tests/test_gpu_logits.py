@@ -127,17 +127,23 @@ def logits_grid(T, N):
     return blocks * -(-N // chunk)
 
 
-@pytest.mark.parametrize("T,H,S,causal", [(2045, 64, 600, False), (1603, 24, 900, True)])
-def test_two_tokens_per_wavefront_shape(T, H, S, causal):
+@pytest.mark.parametrize("T,H,S,causal,slots", [(2045, 64, 600, False, False), (1603, 24, 900, True, False),
+                                                (1037, 40, 1500, True, True)])
+def test_two_tokens_per_wavefront_shape(T, H, S, causal, slots):
     """Calls large enough for the two-token shape, checked in full: a ragged
-    token count, heads not a multiple of 16, causal lengths."""
+    token count, heads not a multiple of 16, causal lengths, a slot list with
+    entries outside the cache."""
     assert logits_grid(T, S) > 512
     rng = np.random.default_rng(T + H)
     q8, w = random_query(T, H, rng)
     codes, scale = random_cache(S, rng)
     lengths = np.clip(np.arange(T) * S // T + 1, 0, S) if causal else None
-    got = run(q8, w, codes, scale, lengths=lengths, stride_pad=3)
-    r = check(got, q8, w, codes, scale, lengths=lengths)
+    key_slots = None
+    if slots:
+        key_slots = rng.permutation(S).astype(np.int64)
+        key_slots[[0, 7, S // 2, S - 1]] = [-1, S, -(1 << 31), (1 << 31) - 1]
+    got = run(q8, w, codes, scale, lengths=lengths, stride_pad=3, key_slots=key_slots)
+    r = check(got, q8, w, codes, scale, lengths=lengths, key_slots=key_slots)
     print("\n[parity] logits two-token shape T=%d H=%d N=%d max err / bound %.3g" % (T, H, S, r), flush=True)
 
 
@@ -158,7 +164,7 @@ def test_key_slots_and_slots_outside_the_cache():
     q8, w = random_query(T, H, rng)
     codes, scale = random_cache(S, rng, row_pad=16)
     slots = rng.permutation(S)[:333].astype(np.int64)
-    slots[[3, 50, 200]] = [-1, S, 1 << 30]                        # read nothing, score 0
+    slots[[3, 50, 200, 201, 332]] = [-1, S, 1 << 30, -(1 << 31), (1 << 31) - 1]   # score 0
     got = run(q8, w, codes, scale, key_slots=slots)
     check(got, q8, w, codes, scale, key_slots=slots)
 
