@@ -75,6 +75,10 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
     // while the position and then the cos/sin row come back -- two dependent
     // round trips instead of three (3-10 % faster on batches of 41-256; the
     // same order on multi-pass items measured 1-9 % slower on large batches).
+    // The multi-pass rows and gate keep their per-lane conditions, though the
+    // compiler waits for each such load inside its branch: issuing them all
+    // unconditionally (heads clamped) made the 64-head, 65536-token call 6 %
+    // slower (279 against 262 us).
     const uint16_t* qt = p.q + t * p.q_st;
     const bool gate_lane = lane < HPI && hbase + lane < p.H;
     uint4 raw[kPasses];
@@ -85,7 +89,7 @@ __device__ __forceinline__ void query_item(const PrepParams& p, int64_t item, in
         raw[0] = load_row<LAYOUT>(qt + (int64_t)min(h0, p.H - 1) * p.q_sh, j);
         wbits = p.w[t * p.w_st + min(hbase + (lane < HPI ? lane : 0), p.H - 1)];
         pos = clamp_position(p.q_pos[t], p.P);
-        rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
+        rl = rope_lane<STYLE, LAYOUT, true>(p, pos, lane);
     } else {
         pos = clamp_position(p.q_pos[t], p.P);
         rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
@@ -146,17 +150,20 @@ __device__ __forceinline__ void query_pair_item(const PrepParams& p, int64_t ite
     auto tok = [&](int ps) -> int64_t { return ps < 2 ? t0 : t1; };
     auto head = [&](int ps) -> int { return 4 * (ps & 1) + g; };
 
-    const int64_t pos0 = clamp_position(p.q_pos[t0], p.P);
-    const int64_t pos1 = clamp_position(p.q_pos[t1], p.P);
-    const RopeLane rl0 = rope_lane<STYLE, LAYOUT>(p, pos0, lane);
-    const RopeLane rl1 = rope_lane<STYLE, LAYOUT>(p, pos1, lane);
+    // The rows and gates first (they depend on nothing), then the positions
+    // and the cos/sin rows they select: two dependent round trips.  Every lane
+    // reads a gate (lanes 16 and up read token t1's, unused), so no load sits
+    // under a per-lane branch.
     uint4 raw[kPasses];
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps)
         raw[ps] = load_row<LAYOUT>(p.q + tok(ps) * p.q_st + (int64_t)head(ps) * p.q_sh, j);
     const int64_t gt = lane < 8 ? t0 : t1;
-    uint32_t wbits = 0;
-    if (lane < 16) wbits = p.w[gt * p.w_st + (lane & 7)];
+    const uint32_t wbits = p.w[gt * p.w_st + (lane & 7)];
+    const int64_t pos0 = clamp_position(p.q_pos[t0], p.P);
+    const int64_t pos1 = clamp_position(p.q_pos[t1], p.P);
+    const RopeLane rl0 = rope_lane<STYLE, LAYOUT>(p, pos0, lane);
+    const RopeLane rl1 = rope_lane<STYLE, LAYOUT>(p, pos1, lane);
 
     int e[kPasses];
 #pragma unroll
@@ -191,13 +198,13 @@ __device__ __forceinline__ void key_item(const PrepParams& p, int64_t item, int 
     const int j = lane & (kLanesPerRow - 1);
     const int64_t t = item * kTokensPerKItem + g;
     const bool valid = t < p.T;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    int64_t pos = 0, slot = -1;
-    if (valid) {
-        raw = load_row<LAYOUT>(p.k + t * p.k_st, j);
-        pos = clamp_position(p.k_pos[t], p.P);
-        slot = p.loc[t];
-    }
+    // a row group past T reads token T - 1 (computed, never stored): no load
+    // under a per-lane branch.  The position first (the cos/sin row waits for
+    // it, and loads retire in issue order), then the row and slot.
+    const int64_t tc = valid ? t : p.T - 1;
+    const int64_t pos = clamp_position(p.k_pos[tc], p.P);
+    const uint4 raw = load_row<LAYOUT>(p.k + tc * p.k_st, j);
+    const int64_t slot = p.loc[tc];
     key_row<STYLE, LAYOUT>(p, valid, raw, pos, slot, lane);
 }
 

@@ -228,10 +228,10 @@ struct RopeLane {
     bool active;       // NeoX: the lane rotates; interleaved: first four values rotate
     bool active_hi;    // interleaved: last four values rotate
     uint32_t mask;     // generic: the lane's elements that rotate
-    int rdim;          // generic: rope_dim
+    int rdim;          // rope_dim (generic layout; interleaved: whether any lane rotates its last four)
 };
 
-template <int STYLE, int LAYOUT>
+template <int STYLE, int LAYOUT, bool LANE_BRANCH = false>
 __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, int lane) {
     RopeLane r;
     const int j = lane & (kLanesPerRow - 1);
@@ -261,6 +261,14 @@ __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, 
         }
         return r;
     }
+    // Every lane loads (a lane outside the rope slice reads the row's first
+    // entries and never uses them): a load under a per-lane condition sits in
+    // a divergent branch, where the compiler waits for it before the branch
+    // ends, holding back every load issued after it.  LANE_BRANCH keeps the
+    // NeoX loads under the lane's condition, for one-pass query items: there
+    // the cos/sin row is the item's last load, nothing queues behind it, and
+    // the branch measured faster (2.03 against 2.19 us for a one-token call,
+    // 2.26 against 2.37 us for 64 tokens).
     if (STYLE == 0) {
         // lanes per half of the rope slice
         const int hl = LAYOUT == kContig ? (R >> 4) : (R >> 3);
@@ -268,10 +276,10 @@ __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, 
         const bool first = j < hl;
         const int pj = first ? j + hl : j - hl;
         r.partner_addr = ((lane & ~(kLanesPerRow - 1)) | (r.active ? pj : j)) << 2;
-        if (r.active) {
+        if (!LANE_BRANCH || r.active) {
             const float sg = first ? -1.0f : 1.0f;
             if (LAYOUT == kContig) {
-                const int base = 8 * (first ? j : j - hl);
+                const int base = r.active ? 8 * (first ? j : j - hl) : 0;
                 const float4 c0 = *reinterpret_cast<const float4*>(crow + base);
                 const float4 c1 = *reinterpret_cast<const float4*>(crow + base + 4);
                 const float4 s0 = *reinterpret_cast<const float4*>(srow + base);
@@ -281,7 +289,7 @@ __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, 
                 r.s[0] = sg * s0.x; r.s[1] = sg * s0.y; r.s[2] = sg * s0.z; r.s[3] = sg * s0.w;
                 r.s[4] = sg * s1.x; r.s[5] = sg * s1.y; r.s[6] = sg * s1.z; r.s[7] = sg * s1.w;
             } else {
-                const int base = 4 * (first ? j : j - hl);
+                const int base = r.active ? 4 * (first ? j : j - hl) : 0;
                 const float4 c0 = *reinterpret_cast<const float4*>(crow + base);
                 const float4 s0 = *reinterpret_cast<const float4*>(srow + base);
                 r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
@@ -291,14 +299,15 @@ __device__ __forceinline__ RopeLane rope_lane(const PrepParams& p, int64_t pos, 
     } else {
         r.active = 4 * j < R;
         r.active_hi = 64 + 4 * j < R;
-        if (r.active) {
-            const float2 c0 = *reinterpret_cast<const float2*>(crow + 2 * j);
-            const float2 s0 = *reinterpret_cast<const float2*>(srow + 2 * j);
-            r.c[0] = c0.x; r.c[1] = c0.y; r.s[0] = s0.x; r.s[1] = s0.y;
-        }
-        if (r.active_hi) {
-            const float2 c1 = *reinterpret_cast<const float2*>(crow + 32 + 2 * j);
-            const float2 s1 = *reinterpret_cast<const float2*>(srow + 32 + 2 * j);
+        const int lo = r.active ? 2 * j : 0;
+        const float2 c0 = *reinterpret_cast<const float2*>(crow + lo);
+        const float2 s0 = *reinterpret_cast<const float2*>(srow + lo);
+        r.c[0] = c0.x; r.c[1] = c0.y; r.s[0] = s0.x; r.s[1] = s0.y;
+        r.c[2] = r.c[3] = r.s[2] = r.s[3] = 0.0f;
+        if (R > 64) {   // the same for every lane: only then does any lane rotate its last four
+            const int hi = r.active_hi ? 32 + 2 * j : 0;
+            const float2 c1 = *reinterpret_cast<const float2*>(crow + hi);
+            const float2 s1 = *reinterpret_cast<const float2*>(srow + hi);
             r.c[2] = c1.x; r.c[3] = c1.y; r.s[2] = s1.x; r.s[3] = s1.y;
         }
     }
@@ -319,15 +328,26 @@ __device__ __forceinline__ void rotate_pair(float& a, float& b, float c, float s
     b = bc + as;
 }
 
-// NeoX rotation of the lane's first N values given the partner's N values.
+// NeoX rotation of the lane's first N values given the partner's N values,
+// on lanes of the rope slice.
 template <int N>
 __device__ __forceinline__ void rotate_neox(float x[8], const float xp[8], const RopeLane& r) {
+    if (!r.active) return;
 #pragma unroll
     for (int m = 0; m < N; ++m) {
         const float xc = x[m] * r.c[m];
         const float ps = xp[m] * r.s[m];
         x[m] = xc + ps;
     }
+}
+
+// One interleaved pair, rotated where `on` (computed on every lane and
+// selected).
+__device__ __forceinline__ void rotate_pair_if(float& a, float& b, float c, float s, bool on) {
+    float ra = a, rb = b;
+    rotate_pair(ra, rb, c, s);
+    a = on ? ra : a;
+    b = on ? rb : b;
 }
 
 // Element-wise RoPE of the generic layout.  Each DPP row of the wavefront
@@ -381,21 +401,19 @@ __device__ __forceinline__ void rope_row(float x[8], const RopeLane& rl) {
 #pragma unroll
             for (int m = 0; m < 8; ++m)
                 xp[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(rl.partner_addr, __float_as_int(x[m])));
-            if (rl.active) rotate_neox<8>(x, xp, rl);
+            rotate_neox<8>(x, xp, rl);
         } else {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 xp[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(rl.partner_addr, __float_as_int(x[m])));
-            if (rl.active) rotate_neox<4>(x, xp, rl);
+            rotate_neox<4>(x, xp, rl);
         }
     } else {
-        if (rl.active) {
-            rotate_pair(x[0], x[1], rl.c[0], rl.s[0]);
-            rotate_pair(x[2], x[3], rl.c[1], rl.s[1]);
-        }
-        if (rl.active_hi) {
-            rotate_pair(x[4], x[5], rl.c[2], rl.s[2]);
-            rotate_pair(x[6], x[7], rl.c[3], rl.s[3]);
+        rotate_pair_if(x[0], x[1], rl.c[0], rl.s[0], rl.active);
+        rotate_pair_if(x[2], x[3], rl.c[1], rl.s[1], rl.active);
+        if (rl.rdim > 64) {
+            rotate_pair_if(x[4], x[5], rl.c[2], rl.s[2], rl.active_hi);
+            rotate_pair_if(x[6], x[7], rl.c[3], rl.s[3], rl.active_hi);
         }
     }
 }
@@ -419,12 +437,10 @@ __device__ __forceinline__ void rope_packed_row(const uint4& raw, float x[8], co
         }
         float xp[8];
         unpack8(pr, xp);
-        if (rl.active) {
-            if (LAYOUT == kContig)
-                rotate_neox<8>(x, xp, rl);
-            else
-                rotate_neox<4>(x, xp, rl);
-        }
+        if (LAYOUT == kContig)
+            rotate_neox<8>(x, xp, rl);
+        else
+            rotate_neox<4>(x, xp, rl);
     } else {
         rope_row<STYLE, LAYOUT>(x, rl);
     }
@@ -433,16 +449,19 @@ __device__ __forceinline__ void rope_packed_row(const uint4& raw, float x[8], co
 // One key row: LayerNorm, RoPE, quantisation and the cache store.  raw holds
 // the lane's eight bf16 values of the row (layout order), pos its clamped
 // table row and slot its cache slot; a row with valid == false computes on
-// whatever it holds and stores nothing.  The caller issues the loads (row
-// first, then position and slot: loads return in issue order).
+// whatever it holds and stores nothing.  The caller issues the loads
+// (position first: the cos/sin row waits for it, and loads retire in issue
+// order; then the row and slot).
 template <int STYLE, int LAYOUT>
 __device__ __forceinline__ void key_row(const PrepParams& p, bool valid, uint4 raw, int64_t pos,
                                         int64_t slot, int lane) {
     const int j = lane & (kLanesPerRow - 1);
-    const RopeLane rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
+    // the LayerNorm parameters first: they depend on nothing, the cos/sin row
+    // on the position
     float gam[8], bet[8];
     load_params<LAYOUT>(p.gamma, j, gam);
     load_params<LAYOUT>(p.beta, j, bet);
+    const RopeLane rl = rope_lane<STYLE, LAYOUT>(p, pos, lane);
 
     float x[8];
     unpack8(raw, x);
