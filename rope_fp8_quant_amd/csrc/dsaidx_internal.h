@@ -42,6 +42,9 @@ struct PrepParams {
     int32_t head_blocks;  // ceil(H / heads_per_item); 1 for two-token items
     int32_t k_blocks;
     int32_t k_first;      // host only: fused small call with key workgroups first
+    int32_t k_period;     // fused 8-head call of several rounds: one key workgroup in every k_period (0: together)
+    uint32_t k_magic;     // workgroup / k_period = (workgroup * k_magic) >> k_shift
+    int32_t k_shift;
     int64_t q_items;      // T * head_blocks, or ceil(T / 2) for two-token items (0: no query work)
     // key rows: item = 4 consecutive tokens
     const uint16_t* k;

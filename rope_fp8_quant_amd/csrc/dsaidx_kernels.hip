@@ -35,7 +35,8 @@
 // items of two tokens x 8 heads (query_pair_item).  A key work item is 4
 // tokens.  Key and query work items share one dispatch: the last k_blocks
 // workgroups take key items (the first ones in small calls of 32 tokens or
-// more: template flag KF).
+// more: the placement template parameter, which also spreads them through
+// the grid in 8-head calls of several rounds).
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
 // is rounded on its own (contraction is off), the LayerNorm sums are fp64, and
@@ -213,7 +214,12 @@ static_assert(256 / 64 <= kXchgWaves, "rope_generic's exchange buffer covers eve
 // The 8-head instantiation is held to six wavefronts per SIMD (80 VGPRs, no
 // spill): 43.0 against 43.7 us at five (92 VGPRs) for 65536 tokens; seven
 // spill (51 us).
-template <int STYLE, int LAYOUT, int HPI, bool KF>
+// Placement of the key workgroups in the grid (template parameter PLACE).
+constexpr int kKeysLast = 0;
+constexpr int kKeysFirst = 1;
+constexpr int kKeysSpread = 2;
+
+template <int STYLE, int LAYOUT, int HPI, int PLACE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HPI == kHeadsPerItemMid ? 6 : 1)))
 void indexer_qk_prep_kernel(PrepParams p) {
     const int lane = threadIdx.x & 63;
@@ -222,21 +228,41 @@ void indexer_qk_prep_kernel(PrepParams p) {
     const int64_t nblocks = gridDim.x;
     const int64_t b = blockIdx.x;
     const int64_t nq = nblocks - p.k_blocks;
-#if DSAIDX_K_PLACEMENT == 2
-    const int64_t k_before = b * p.k_blocks / nblocks;
-    const bool is_key = (b + 1) * p.k_blocks / nblocks > k_before;
-    const int64_t kb = k_before, qb = b - k_before;
-#elif DSAIDX_K_PLACEMENT == 1
-    // key workgroups last (their LayerNorm work overlaps the query stream's
-    // tail), or first (KF) in small calls of 32 tokens or more, where the key
-    // rows' longer chain of dependent steps is the critical path (64 tokens:
-    // 2.46 against 2.57 us per call; with fewer tokens the query rows are)
-    const bool is_key = KF ? b < p.k_blocks : b >= nq;
-    const int64_t kb = KF ? b : b - nq, qb = KF ? b - p.k_blocks : b;
-#else
-    const bool is_key = b < p.k_blocks;
-    const int64_t kb = b, qb = b - p.k_blocks;
-#endif
+    // Where the key workgroups sit.  Calls of several rounds at 8 heads
+    // (kKeysSpread) spread them evenly through the grid, one in every
+    // k_period workgroups, so that their VALU-bound rows (LayerNorm, RoPE,
+    // quantisation: a sixth of the bytes there) overlap the query rows'
+    // memory stream.  Otherwise they come last (their work overlaps the query
+    // stream's tail), or first (kKeysFirst) in small calls of 32 tokens or
+    // more, where the key rows' longer chain of dependent steps is the
+    // critical path (64 tokens: 2.46 against 2.57 us per call; with fewer
+    // tokens the query rows are).  A template parameter, not a branch: the
+    // branch and its parameters alone cost the small calls 0.1 us.
+    bool is_key;
+    int64_t kb, qb;
+    if constexpr (PLACE == kKeysSpread) {
+        // workgroup b = j * k_period + i: for j < k_blocks the last of each
+        // period (i = k_period - 1) is key workgroup j and the rest query
+        // workgroups; past k_blocks periods, query workgroups only.  The grid
+        // is below 2^25 workgroups, within the magic division's range.
+        const uint32_t bb = (uint32_t)b, per = (uint32_t)p.k_period;
+        const uint32_t j = (uint32_t)(((uint64_t)bb * p.k_magic) >> p.k_shift);
+        const uint32_t i = bb - j * per;
+        if (j < (uint32_t)p.k_blocks) {
+            is_key = i == per - 1;
+            kb = j;
+            qb = (int64_t)j * (per - 1) + i;
+        } else {
+            is_key = false;
+            kb = 0;
+            qb = (int64_t)p.k_blocks * (per - 1) + (bb - (uint32_t)p.k_blocks * per);
+        }
+    } else {
+        constexpr bool kFirst = PLACE == kKeysFirst;
+        is_key = kFirst ? b < p.k_blocks : b >= nq;
+        kb = kFirst ? b : b - nq;
+        qb = kFirst ? b - p.k_blocks : b;
+    }
     if (is_key) {
         const int64_t stride = (int64_t)p.k_blocks * waves;
         for (int64_t it = kb * waves + wave; it < p.k_items; it += stride)
@@ -287,39 +313,44 @@ hipError_t launch_prep(const PrepParams& p, int style, unsigned grid, unsigned b
     void* args[] = {&copy};
     const int hpi = p.heads_per_item;
     const bool kf = p.k_first != 0 && hpi == kHeadsPerItemSmall;
-    auto pick = [hpi, kf](auto k4f, auto k4, auto k8, auto k16) -> const void* {
+    const bool spread = p.k_period > 0 && hpi == kHeadsPerItemMid;
+    auto pick = [hpi, kf, spread](auto k4f, auto k4, auto k8s, auto k8, auto k16) -> const void* {
         return hpi == kHeadsPerItemSmall ? (kf ? reinterpret_cast<const void*>(k4f)
                                                : reinterpret_cast<const void*>(k4))
-               : hpi == kHeadsPerItemMid ? reinterpret_cast<const void*>(k8)
+               : hpi == kHeadsPerItemMid ? (spread ? reinterpret_cast<const void*>(k8s)
+                                                   : reinterpret_cast<const void*>(k8))
                                          : reinterpret_cast<const void*>(k16);
     };
     const void* fn;
     if (p.generic)
         fn = style == 1 ? (hpi == kHeadsPerItemSmall
                                ? reinterpret_cast<const void*>(
-                                     &indexer_qk_prep_kernel<1, kGeneric, kHeadsPerItemSmall, false>)
+                                     &indexer_qk_prep_kernel<1, kGeneric, kHeadsPerItemSmall, kKeysLast>)
                                : reinterpret_cast<const void*>(
-                                     &indexer_qk_prep_kernel<1, kGeneric, kHeadsPerItem, false>))
+                                     &indexer_qk_prep_kernel<1, kGeneric, kHeadsPerItem, kKeysLast>))
                         : (hpi == kHeadsPerItemSmall
                                ? reinterpret_cast<const void*>(
-                                     &indexer_qk_prep_kernel<0, kGeneric, kHeadsPerItemSmall, false>)
+                                     &indexer_qk_prep_kernel<0, kGeneric, kHeadsPerItemSmall, kKeysLast>)
                                : reinterpret_cast<const void*>(
-                                     &indexer_qk_prep_kernel<0, kGeneric, kHeadsPerItem, false>));
+                                     &indexer_qk_prep_kernel<0, kGeneric, kHeadsPerItem, kKeysLast>));
     else if (style == 1)
-        fn = pick(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, true>,
-                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, false>,
-                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid, false>,
-                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem, false>);
+        fn = pick(&indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, kKeysFirst>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemSmall, kKeysLast>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid, kKeysSpread>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItemMid, kKeysLast>,
+                  &indexer_qk_prep_kernel<1, kSplit, kHeadsPerItem, kKeysLast>);
     else if (p.R <= 64)
-        fn = pick(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall, true>,
-                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall, false>,
-                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemMid, false>,
-                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem, false>);
+        fn = pick(&indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall, kKeysFirst>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemSmall, kKeysLast>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemMid, kKeysSpread>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItemMid, kKeysLast>,
+                  &indexer_qk_prep_kernel<0, kSplit, kHeadsPerItem, kKeysLast>);
     else
-        fn = pick(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall, true>,
-                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall, false>,
-                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemMid, false>,
-                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItem, false>);
+        fn = pick(&indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall, kKeysFirst>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemSmall, kKeysLast>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemMid, kKeysSpread>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItemMid, kKeysLast>,
+                  &indexer_qk_prep_kernel<0, kContig, kHeadsPerItem, kKeysLast>);
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream);
 }
 

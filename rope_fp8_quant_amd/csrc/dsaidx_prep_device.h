@@ -22,14 +22,6 @@
 #define DSAIDX_NT_STORES 1
 #endif
 
-// Placement of the key workgroups of a fused dispatch: 0 first, 1 last,
-// 2 spread evenly among the query workgroups.  Last measures best: the query
-// stream starts at once and the latency-bound LayerNorm work of the key rows
-// overlaps its tail.
-#ifndef DSAIDX_K_PLACEMENT
-#define DSAIDX_K_PLACEMENT 1
-#endif
-
 namespace dsaidx {
 namespace {
 

@@ -248,6 +248,7 @@ void launch_shapes() {
         CHECK(l.p.T == 5 && l.p.H == 64 && l.p.R == 64 && l.p.P == 4096 && l.p.rs == 32);
         CHECK(l.p.page_size == 0 && l.p.S == 4096 && l.p.eps == 1e-6f && l.p.q_scale == nullptr);
         CHECK(l.p.k_first == 0);                 // fewer than 32 tokens: key workgroups last
+        CHECK(l.p.k_period == 0);
     }
     // fused, small batch of 64 tokens: key workgroups first, none capped
     {
@@ -281,6 +282,46 @@ void launch_shapes() {
         const Launch& l = g_launches[0];
         CHECK(l.p.heads_per_item == 8 && l.p.head_blocks == 1 && l.p.q_items == 2049);
         CHECK(l.p.k_items == 1025 && l.p.k_blocks == 257 && l.grid == 513 + 257);
+        CHECK(l.p.k_period == 0);                // one resident round: key workgroups last
+    }
+    // fused 8-head calls of several rounds: key workgroups spread through the grid.
+    // The kernel's split of the workgroup index (one key workgroup at the end
+    // of each period, query workgroups past the last period) must give every
+    // key and query workgroup index exactly once.
+    for (const auto& shape : {std::pair<int64_t, int32_t>{65536, 8}, {30001, 8}, {20000, 8}}) {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(shape.first, shape.second);
+        dsaidx_k_args k = make_k(shape.first);
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1);
+        const Launch& l = g_launches[0];
+        CHECK(l.p.k_period >= 2 && l.p.k_blocks > 0);
+        if (l.p.k_period < 2 || l.p.k_blocks <= 0) continue;
+        const uint32_t per = (uint32_t)l.p.k_period, kbn = (uint32_t)l.p.k_blocks;
+        const uint32_t nq = l.grid - kbn;
+        std::vector<int> seen_k(kbn, 0), seen_q(nq, 0);
+        for (uint32_t b = 0; b < l.grid; ++b) {
+            const uint32_t j = (uint32_t)(((uint64_t)b * l.p.k_magic) >> l.p.k_shift);
+            CHECK(j == b / per);
+            const uint32_t i = b - j * per;
+            if (j < kbn && i == per - 1) {
+                ++seen_k[j];
+            } else {
+                const uint64_t qb = j < kbn ? (uint64_t)j * (per - 1) + i : (uint64_t)kbn * (per - 1) + (b - kbn * per);
+                CHECK(qb < nq);
+                if (qb < nq) ++seen_q[qb];
+            }
+        }
+        for (int c : seen_k) CHECK(c == 1);
+        for (int c : seen_q) CHECK(c == 1);
+    }
+    // at 64 heads the key workgroups stay last whatever the size
+    for (int64_t T : {8192, 65536}) {
+        g_launches.clear();
+        dsaidx_q_args q = make_q(T, 64);
+        dsaidx_k_args k = make_k(T);
+        CHECK(dsaidx_qk_fused(&q, &k, &rope, nullptr) == DSAIDX_OK);
+        CHECK(g_launches.size() == 1 && g_launches[0].p.k_period == 0);
     }
     // query side alone, interleaved rope, odd head count
     {
