@@ -129,11 +129,14 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
+// (mov_dpp rather than update_dpp with an old value: every lane is enabled
+// and row_ror reads inside the row, so no old value is ever kept, and none
+// has to be written into the destination first.)
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xFFFFFFFFull), CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(u & 0xFFFFFFFFull), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), CTRL, 0xF, 0xF, true);
     return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
 }
 
@@ -468,7 +471,9 @@ __device__ __forceinline__ void key_row(const PrepParams& p, bool valid, uint4 r
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         d[m] = x[m] - mu;
-        s2 += (double)d[m] * (double)d[m];
+        // the product of two fp32 values is exact in fp64, so one fused
+        // multiply-add rounds exactly as the product and the sum did
+        s2 = __builtin_fma((double)d[m], (double)d[m], s2);
     }
     s2 = row_sum(s2);
     const float var = (float)(s2 * (1.0 / kRow));
