@@ -256,6 +256,23 @@ def test_head_counts_large_batches(H, style, rope_dim):
     assert np.array_equal(out2["q_fp8"], out["q_fp8"]) and np.array_equal(out2["w_out"], out["w_out"])
 
 
+@pytest.mark.parametrize("T,style", [(12001, W.NEOX), (20000, W.INTERLEAVED)])
+def test_eight_heads_with_spread_key_workgroups(T, style):
+    """8-head calls of several resident rounds spread the key workgroups
+    through the grid (one in every k_period workgroups, query workgroups
+    past the last period): every query and key row checked against the
+    oracle, with a lone last token in the two-token items."""
+    print("\n[case] 8 heads, spread key workgroups, T=%d style=%d" % (T, style), flush=True)
+    wl = W.make(T, 8, style=style, table_rows=32768, num_slots=T + 333, slot_mode="perm_prefix",
+                seed=9000 + T)
+    c = DeviceCase(wl)
+    c.run("fused")
+    out = c.host()
+    rep = {}
+    check_q(out, wl, rep)
+    check_k(out, wl, rep)
+
+
 def test_two_token_items_on_strided_views():
     """8 heads in a large batch (items of two tokens x 8 heads) with a padded
     head stride and k / weights as column slices of one [T, 128 + H] buffer:
