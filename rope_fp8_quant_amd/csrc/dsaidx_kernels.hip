@@ -39,7 +39,8 @@
 // the grid in 8-head calls of several rounds).
 //
 // Arithmetic matches the definition row for row: every fp32 product and sum
-// is rounded on its own (contraction is off), the LayerNorm sums are fp64, and
+// is rounded on its own (contraction is off), the LayerNorm sums are fp64 (the
+// variance sum by fused multiply-adds, whose fp32-by-fp32 products are exact), and
 // the codes come from the gfx950 scaled packed convert, which rounds x / 2^e
 // to nearest-even E4M3FN -- the same as multiplying by 2^-e (exact) and
 // converting.  No value can exceed 448, as 2^e is chosen from the row max.

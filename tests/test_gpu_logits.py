@@ -158,6 +158,27 @@ def test_causal_lengths_and_ragged_edges():
     check(got, q8, w, codes, scale, lengths=lengths)
 
 
+@pytest.mark.parametrize("T,H,S", [(61, 48, 9000), (64, 64, 16384)])
+def test_one_token_shape_ragged_lengths_over_many_chunks(T, H, S):
+    """One-token shape with many chunks (a workgroup's keys are every
+    chunks-th 16-key block), checked in full: every token a different length
+    (zero, negative, multiples of 16 and their neighbours, N, past N), a slot
+    list with entries outside the cache, N not a multiple of 16 in the first
+    case."""
+    assert logits_grid(T, S) <= 512 and -(-S // 256) >= 32
+    rng = np.random.default_rng(T * 7 + S)
+    q8, w = random_query(T, H, rng)
+    codes, scale = random_cache(S, rng)
+    lengths = rng.integers(-5, S + 100, size=T)
+    lengths[:10] = [0, -1, 1, 15, 16, 17, S - 1, S, 4096, 4097]
+    slots = rng.permutation(S).astype(np.int64)
+    slots[[2, 99, S // 3, S - 2]] = [-1, S, -(1 << 31), (1 << 31) - 1]
+    got = run(q8, w, codes, scale, key_slots=slots, lengths=lengths, stride_pad=7)
+    r = check(got, q8, w, codes, scale, key_slots=slots, lengths=lengths)
+    print("\n[parity] logits one-token shape T=%d H=%d N=%d ragged max err / bound %.3g" % (T, H, S, r),
+          flush=True)
+
+
 def test_key_slots_and_slots_outside_the_cache():
     rng = np.random.default_rng(6)
     T, H, S = 24, 64, 500
