@@ -249,10 +249,10 @@ dsaidx_status dsaidx_k_only_prepare_store(const dsaidx_k_args* k, const dsaidx_r
  * The products are exact in fp32 and the sums are fp32 in an order the
  * library chooses; the bf16 rounding is to nearest even.
  *   hidden         bf16 [T, d]: token t at hidden + t * hidden_stride_t; 16-byte
- *                  aligned; hidden_stride_t >= d, a multiple of 8
+ *                  aligned; hidden_stride_t >= d, a multiple of 8, at most 2^22
  *   weight         bf16 [128 + H, d] (a Linear layer's [out, in] layout): row n
  *                  at weight + n * weight_stride_n; 16-byte aligned;
- *                  weight_stride_n >= d, a multiple of 8
+ *                  weight_stride_n >= d, a multiple of 8, at most 2^22
  *   hidden_dim     d: a multiple of 64 in [64, 2^20]
  *   num_heads      H in [1, 64]
  *   gates_out      out: bf16 [T, H], token stride gates_stride_t >= H; 2-byte aligned

@@ -294,7 +294,7 @@ dsaidx_status dsaidx_qk_fused(const dsaidx_q_args* q, const dsaidx_k_args* k,
     const int64_t kcap = p.heads_per_item == dsaidx::kHeadsPerItem
                              ? ceil_div(qb, kKeyBlockDivisor) : capped_grid(p.k_items, kBlock);
     if (kb > kcap) kb = kcap;
-    // small calls of 32 tokens or more: key workgroups first (the kernel's KF)
+    // small calls of 32 tokens or more: key workgroups first (the kernel's kKeysFirst placement)
     p.k_first = (p.heads_per_item == dsaidx::kHeadsPerItemSmall && p.T >= 32) ? 1 : 0;
 
     p.k_blocks = (int32_t)kb;
@@ -323,9 +323,13 @@ dsaidx_status dsaidx_proj_k_norm_rope_quant_store(const dsaidx_proj_args* j, con
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (j->num_heads < 1 || j->num_heads > dsaidx::kProjMaxHeads || j->reserved != 0)
         return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (!j->hidden || !aligned(j->hidden, 16) || j->hidden_stride_t < d || j->hidden_stride_t % 8 != 0)
+    // row strides of at most 2^22 elements keep the kernel's byte offsets
+    // within a workgroup's 256 hidden rows, and within the weight, below 2^31
+    if (!j->hidden || !aligned(j->hidden, 16) || j->hidden_stride_t < d || j->hidden_stride_t % 8 != 0 ||
+        j->hidden_stride_t > (int64_t(1) << 22))
         return DSAIDX_ERR_INVALID_ARGUMENT;
-    if (!j->weight || !aligned(j->weight, 16) || j->weight_stride_n < d || j->weight_stride_n % 8 != 0)
+    if (!j->weight || !aligned(j->weight, 16) || j->weight_stride_n < d || j->weight_stride_n % 8 != 0 ||
+        j->weight_stride_n > (int64_t(1) << 22))
         return DSAIDX_ERR_INVALID_ARGUMENT;
     if (!j->gates_out || !aligned(j->gates_out, 2) || j->gates_stride_t < j->num_heads)
         return DSAIDX_ERR_INVALID_ARGUMENT;

@@ -22,7 +22,8 @@
 // 32 x 16 columns):
 //   - hidden rows go straight from HBM into the A operands (16 bytes per lane,
 //     lane l: token l % 16, elements 8 (l / 16) ..), nontemporal: every
-//     element is read once;
+//     element is read once; as raw buffer loads from a per-workgroup base,
+//     each address is one 32-bit register plus a scalar stage offset;
 //   - the stage's weight slice (192 rows x 128 bytes) goes through LDS,
 //     double-buffered, one barrier per stage; its rows are 144 bytes apart so
 //     that the 16 lanes of a B-operand read hit distinct banks;
@@ -30,6 +31,10 @@
 //     fp32, with each weight operand read from LDS a few operands ahead
 //     (the order is pinned with scheduling groups: the compiler otherwise
 //     reads each operand just before its MFMAs).
+// The first stage starts the accumulators with zero as the MFMAs' C operand:
+// zeroing them beforehand gives 192 accumulators one shared zero register, and
+// the register allocator then rotates them through spare registers inside
+// the loop (about 150 copies per 192 MFMAs).
 // Each stage first issues the next stage's weight slice and hidden rows; the
 // stage ends with an LDS-only wait and a bare barrier, so the hidden rows stay
 // in flight across it.  The weight (0.3 % of the bytes at d = 7168) is re-read
@@ -51,6 +56,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = kProjThreads;
 constexpr int kColBlocks = kProjMaxCols / 16;        // 12 blocks of 16 output columns
 constexpr int kStageK = kProjStageK;                 // hidden elements per stage (64)
+constexpr int kKSteps = kStageK / 32;                // MFMA k steps per stage
+constexpr int kWChunks = kStageK / 8;                // 16-byte chunks of a weight row's stage slice
+constexpr int kWRowsPerPass = kThreads / kWChunks;   // weight rows staged per pass of the workgroup
+constexpr int kWPer = kProjMaxCols / kWRowsPerPass;  // weight chunks staged per thread and stage
+static_assert(kWPer * kWRowsPerPass == kProjMaxCols, "weight staging covers the rows");
 constexpr int kWPitch = kStageK * 2 + 16;            // LDS bytes per weight row (144)
 constexpr int kWStageBytes = kProjMaxCols * kWPitch;   // 27648
 constexpr int kKPitch = kRow * 2 + 16;               // LDS bytes per staged key row (272)
@@ -71,11 +81,7 @@ __device__ __forceinline__ uint4 lds_row(const uint8_t* row, int j) {
     return make_uint4(a.x, a.y, b.x, b.y);
 }
 
-__device__ __forceinline__ uint4 load16_keep(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-
-typedef uint4 ARows[4][2];   // a wavefront's hidden-row operands of one stage: [row block][k half]
+typedef uint4 ARows[4][kKSteps];   // a wavefront's hidden-row operands of one stage: [row block][k step]
 
 #ifndef DSAIDX_PROJ_AHEAD_B
 #define DSAIDX_PROJ_AHEAD_B 4
@@ -99,8 +105,8 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15;          // MFMA operand row / column within a block
     const int lq = lane >> 4;          // MFMA operand k group (8 elements)
-    const int wc = tid & 7;            // weight staging: 16-byte chunk of a row's stage slice
-    const int wr0 = tid >> 3;          //   and first row (rows wr0 + 32 j)
+    const int wc = tid % kWChunks;     // weight staging: 16-byte chunk of a row's stage slice
+    const int wr0 = tid / kWChunks;    //   and first row (rows wr0 + kWRowsPerPass j)
     const int64_t T = a.prep.T;
     const int stages = a.d / kStageK;
 
@@ -109,40 +115,45 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
         // Operand rows, clamped: a token past T reads row T - 1 and a column
         // past 128 + H reads the last weight row (their results are never
         // stored), so every load below is unconditional and the compiler's
-        // waits stay exact.
-        const uint16_t* arow[4];
+        // waits stay exact.  Byte offsets are 32-bit: the host bounds both
+        // row strides by 2^22 elements.
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.x + row0 * a.x_st), 0, -1, 0x00020000);
+        const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.w), 0, -1, 0x00020000);
+        uint32_t aoff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t t = row0 + 64 * wave + 16 * i + lr;
-            arow[i] = a.x + (t < T ? t : T - 1) * a.x_st + 8 * lq;
+            aoff[i] = (uint32_t)(((t < T ? t : T - 1) - row0) * a.x_st * 2) + 16u * lq;
         }
-        const uint16_t* wrow[6];
+        uint32_t woff[kWPer];
 #pragma unroll
-        for (int jj = 0; jj < 6; ++jj) {
-            const int n = wr0 + 32 * jj;
-            wrow[jj] = a.w + (int64_t)(n < a.n_out ? n : a.n_out - 1) * a.w_st + 8 * wc;
+        for (int jj = 0; jj < kWPer; ++jj) {
+            const int n = wr0 + kWRowsPerPass * jj;
+            woff[jj] = (uint32_t)((n < a.n_out ? n : a.n_out - 1) * a.w_st * 2) + 16u * wc;
         }
         f32x4 acc[4][kColBlocks];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int cb = 0; cb < kColBlocks; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         auto fetch_a = [&](int s, ARows& x) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) x[i][ks] = load16(arow[i] + s * kStageK + 32 * ks);
+                for (int ks = 0; ks < kKSteps; ++ks)
+                    x[i][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                        xrs, aoff[i] + 64 * ks, 2 * kStageK * s, 2));
         };
-        auto fetch_w = [&](int s, uint4 (&w)[6]) {
+        auto fetch_w = [&](int s, uint4 (&w)[kWPer]) {
 #pragma unroll
-            for (int jj = 0; jj < 6; ++jj) w[jj] = load16_keep(wrow[jj] + s * kStageK);
+            for (int jj = 0; jj < kWPer; ++jj)
+                w[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    wrs, woff[jj], 2 * kStageK * s, 0));
         };
-        auto store_w = [&](int buf, const uint4 (&w)[6]) {
+        auto store_w = [&](int buf, const uint4 (&w)[kWPer]) {
             uint8_t* base = smem + buf * kWStageBytes + 16 * wc;
 #pragma unroll
-            for (int jj = 0; jj < 6; ++jj)
-                *reinterpret_cast<uint4*>(base + (wr0 + 32 * jj) * kWPitch) = w[jj];
+            for (int jj = 0; jj < kWPer; ++jj)
+                *reinterpret_cast<uint4*>(base + (wr0 + kWRowsPerPass * jj) * kWPitch) = w[jj];
         };
         // Stage s: the weight slice and the hidden rows of stage s + 1 are
         // issued (the weight first), the MFMAs of stage s run on `cur` and
@@ -150,17 +161,16 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
         // operands before its MFMAs, and the next weight slice goes to the
         // other buffer before the stage's one barrier.  The last stage
         // re-fetches itself instead of branching.
-        auto stage = [&](int s, const ARows& cur, ARows& fut) {
-            uint4 wn[6];
-            const int nx = s + 1 < stages ? s + 1 : s;
-            fetch_w(nx, wn);
-            fetch_a(nx, fut);
+        auto stage = [&](int s, const ARows& cur, ARows& fut, bool first) {
+            uint4 wn[kWPer];
+            fetch_w(s + 1 < stages ? s + 1 : s, wn);
+            fetch_a(s + 1 < stages ? s + 1 : s, fut);
             const uint8_t* wb = smem + (s & 1) * kWStageBytes + lr * kWPitch + 16 * lq;
-            auto bread = [&](int o) -> uint4 {       // operand o = 12 ks + cb
+            auto bread = [&](int o) -> uint4 {       // operand o = kColBlocks ks + cb
                 return *reinterpret_cast<const uint4*>(wb + (o % kColBlocks) * 16 * kWPitch +
                                                        64 * (o / kColBlocks));
             };
-            constexpr int kOps = 2 * kColBlocks;
+            constexpr int kOps = kKSteps * kColBlocks;
             uint4 bq[kAheadB];
 #pragma unroll
             for (int o = 0; o < kAheadB; ++o) bq[o] = bread(o);
@@ -171,13 +181,14 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
                 if (o + kAheadB < kOps) bq[o % kAheadB] = bread(o + kAheadB);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur[i][ks]), b,
-                                                                          acc[i][cb], 0, 0, 0);
+                    acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, cur[i][ks]), b,
+                        first && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][cb], 0, 0, 0);
             }
             // the order above, kept by the scheduler: the stage's global loads,
             // the first kAheadB weight reads, then the four MFMAs of each
             // operand with the next operand's read
-            __builtin_amdgcn_sched_group_barrier(0x020, 14, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, kWPer + 4 * kKSteps, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, kAheadB, 0);
 #pragma unroll
             for (int o = kAheadB; o < kOps; ++o) {
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
 
         ARows A0, A1;
         {
-            uint4 w0[6];
+            uint4 w0[kWPer];
             fetch_w(0, w0);
             fetch_a(0, A0);
             store_w(0, w0);
@@ -200,12 +211,13 @@ __global__ __launch_bounds__(kThreads, 1) void proj_key_prep_kernel(ProjParams a
         // two stages per iteration alternate the operand sets; an odd last
         // stage runs after the loop, so that its body has no branches (they
         // would make the compiler's waits conservative)
-        int s = 0;
+        stage(0, A0, A1, true);
+        int s = 1;
         for (; s + 2 <= stages; s += 2) {
-            stage(s, A0, A1);
-            stage(s + 1, A1, A0);
+            stage(s, A1, A0, false);
+            stage(s + 1, A0, A1, false);
         }
-        if (s < stages) stage(s, A0, A1);
+        if (s < stages) stage(s, A1, A0, false);
         __syncthreads();
 
         // Epilogue 1: the projection's output rounded to bf16 (nearest even),

@@ -749,6 +749,14 @@ void projection_calls() {
     dsaidx_proj_args j = proj(7168, 64);
     CHECK(dsaidx_proj_k_norm_rope_quant_store(&j, &k, &rope, nullptr) == DSAIDX_OK);
     CHECK(g_launches.size() == 1 && g_launches[0].kind == 5);
+    {   // the largest row strides accepted
+        dsaidx_proj_args jw = proj(7168, 64);
+        jw.hidden_stride_t = int64_t(1) << 22;
+        jw.weight_stride_n = int64_t(1) << 22;
+        CHECK(dsaidx_proj_k_norm_rope_quant_store(&jw, &k, &rope, nullptr) == DSAIDX_OK);
+        g_launches.clear();
+        CHECK(dsaidx_proj_k_norm_rope_quant_store(&j, &k, &rope, nullptr) == DSAIDX_OK);
+    }
     if (!g_launches.empty()) {
         const Launch& l = g_launches[0];
         const int64_t blocks = (300 + dsaidx::kProjRows - 1) / dsaidx::kProjRows;
@@ -774,6 +782,8 @@ void projection_calls() {
     bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.num_heads = 65; });
     bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.hidden = nullptr; });
     bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.weight_stride_n = 7000; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.hidden_stride_t = (int64_t(1) << 22) + 8; });
+    bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.weight_stride_n = (int64_t(1) << 22) + 8; });
     bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.gates_stride_t = 32; });
     bad([](dsaidx_proj_args& j, dsaidx_k_args&) { j.k_out = at<uint16_t>(8); j.k_out_stride_t = 128; });
     bad([](dsaidx_proj_args&, dsaidx_k_args& k) { k.ln_eps = 0.0f; });

@@ -357,6 +357,7 @@ BAD_PROJ = [dict(hidden=None), dict(weight=None), dict(gates_out=None), dict(hid
             dict(weight=FAKE + 8), dict(gates_out=FAKE + 1), dict(k_out=FAKE + 8),
             dict(hidden_dim=0), dict(hidden_dim=32), dict(hidden_dim=96), dict(hidden_dim=7168 + 32), dict(hidden_dim=1 << 21),
             dict(hidden_stride_t=7160), dict(hidden_stride_t=7172), dict(weight_stride_n=7160),
+            dict(hidden_stride_t=(1 << 22) + 8), dict(weight_stride_n=(1 << 22) + 8),
             dict(weight_stride_n=7172), dict(num_heads=0), dict(num_heads=65), dict(reserved=1),
             dict(gates_stride_t=63), dict(k_out=FAKE, k_out_stride_t=120),
             dict(k_out=FAKE, k_out_stride_t=132)]
