@@ -479,7 +479,12 @@ dsaidx_status dsaidx_mqa_logits(const dsaidx_logits_args* a, dsaidx_stream_t str
     // for 64 tokens x 16384 keys); larger calls keep two tokens per
     // wavefront, which reads each key operand for twice the MFMAs (285-293
     // against 275-281 us on the causal 8192-token prefill).
-    p.tokens_per_wave = blocks * chunks <= kLogitsOneRound ? 1 : 2;
+    // The one-token kernel takes 16 blocks of 16 keys per workgroup, spread
+    // over the key range at a stride of `chunks` blocks: they cover the keys
+    // when 256 * chunks >= N (always so in one round, whose chunks hold at
+    // most 256 keys).
+    p.tokens_per_wave = blocks * chunks <= kLogitsOneRound &&
+                        chunks * 2 * dsaidx::kLogitsStageKeys >= a->num_keys ? 1 : 2;
     return to_status(dsaidx::launch_logits(p, reinterpret_cast<hipStream_t>(stream)));
 }
 

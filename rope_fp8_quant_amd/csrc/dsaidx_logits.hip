@@ -18,11 +18,15 @@
 // Work: a workgroup takes 8 query tokens (their q rows and gates held in
 // registers for the whole call) and one chunk of keys: 4 wavefronts of 2
 // tokens, or, for calls whose grid is one resident round (decode), 8
-// wavefronts of 1 token, which hold four wavefronts per SIMD and issue each
-// block's MFMAs before the previous block's epilogue.  Keys are staged
-// through LDS 128 at a time (double-buffered, one barrier per stage; each
+// wavefronts of 1 token.  Keys are staged through LDS 128 at a time (each
 // thread brings 32 bytes of one or two key rows), so each 16-key block read
-// from L2 feeds 8 tokens x 4 head blocks of MFMAs.  Per
+// from L2 feeds 8 tokens x 4 head blocks of MFMAs.  Two tokens per wavefront:
+// double-buffered stages, one barrier per stage.  One token per wavefront:
+// four wavefronts per SIMD; the workgroup's 256 keys are 16-key blocks
+// spread over the whole key range, both stages go to LDS behind one barrier,
+// and each wavefront then runs through its blocks on its own, stopping at its
+// token's length and issuing each block's MFMAs before the previous block's
+// epilogue.  Per
 // block (two tokens): the 8 MFMAs of a wavefront, the next block's key
 // operand read from LDS behind them, then ReLU and gate on the 4 results of
 // each lane, a sum over the lane groups for both tokens together (two
@@ -58,7 +62,6 @@ struct LgShape {
     static constexpr int kKPT = kLgStage / (kThreads / 4);
     static_assert(kKPT * (kThreads / 4) == kLgStage, "stage rows per thread");
     static constexpr int kMinWaves = TPW == 2 ? 3 : 4;
-    static constexpr bool kReadAhead = TPW == 2;
 };
 
 // 16 x 16 x 128 block of dots over E4M3 codes (format 0 for both operands,
@@ -123,19 +126,38 @@ void mqa_logits_kernel(LogitsParams p) {
     // chunk's keys on one XCD when there are few token blocks and many chunks.
     const uint32_t bx = blockIdx.x;
     const uint32_t qd = (uint32_t)(((uint64_t)bx * p.grid_magic) >> p.grid_shift);
-    int tb, key0;
+    int tb, ci;    // token block, chunk
     if (p.chunk_major) {
         tb = p.blocks - 1 - (int)(bx - qd * (uint32_t)p.blocks);
-        key0 = (int)qd * p.chunk;
+        ci = (int)qd;
     } else {
         tb = p.blocks - 1 - (int)qd;
-        key0 = (int)(bx - qd * (uint32_t)p.chunks) * p.chunk;
+        ci = (int)(bx - qd * (uint32_t)p.chunks);
     }
     const int t_first = tb * TPB;
 
+    // The workgroup's keys.  Two tokens per wavefront: chunk ci's contiguous
+    // keys [key0, key0 + chunk).  One token per wavefront (a call of one
+    // resident round): the 16 blocks of 16 keys ci, ci + chunks, ci + 2 chunks,
+    // ... ci + 15 chunks, so that every workgroup holds keys from the whole
+    // range; under ragged lengths each wavefront skips the blocks at or past
+    // its own token's length, and no compute unit is left with only the first
+    // keys, which every token still needs.  The host takes this shape only
+    // when chunks <= 512 and 256 chunks >= N, so those blocks cover every key
+    // and N <= 2^17: the key arithmetic stays far inside 32 bits.
+    constexpr bool kStrided = TPW == 1;
+    const int key0 = kStrided ? 0 : ci * p.chunk;
+    // key of row r (0 <= r < kLgStage) of the workgroup's stage st
+    auto key_of = [&](int st, int r) -> int {
+        if constexpr (kStrided)
+            return 16 * (ci + p.chunks * (st * (kLgStage / 16) + (r >> 4))) + (r & 15);
+        else
+            return key0 + st * kLgStage + r;
+    };
+
     constexpr int KPT = LgShape<TPW>::kKPT;
     const int sk = tid >> 2, sp = tid & 3;
-    const int key1 = p.N - key0 < p.chunk ? p.N : key0 + p.chunk;
+    const int key1 = kStrided || p.N - key0 < p.chunk ? p.N : key0 + p.chunk;
 
     // Set-up loads.  Each reads a clamped, valid address (the host checks T,
     // N, S >= 1 and 1 <= H <= 64) and is masked where it is used: a load
@@ -163,14 +185,13 @@ void mqa_logits_kernel(LogitsParams p) {
         for (int i = 0; i < TPB; ++i) kmax = max(kmax, length_of(i));
         return min(key1, kmax);
     };
-    // slot-list entries of the stage at s0, as read (slot_of drops the
-    // entries at or past kend when the rows are fetched, and ignores them
-    // without a slot list)
-    auto slots_at = [&](int s0, int32_t (&out)[KPT]) {
+    // slot-list entries of stage st, as read (slot_ok drops the entries at or
+    // past kend when the rows are fetched)
+    auto slots_at = [&](int st, int32_t (&out)[KPT]) {
         if constexpr (!SLOTS) return;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const int s = s0 + 64 * j + sk;
+            const int s = key_of(st, 64 * j + sk);
             out[j] = p.key_slots[min(s, p.N - 1)];
         }
     };
@@ -181,11 +202,11 @@ void mqa_logits_kernel(LogitsParams p) {
     constexpr bool kEarlyLoads = TPW == 1;
     if constexpr (!kEarlyLoads) {
         kend = chunk_end();
-        if (kend <= key0) return;
+        if (kend <= key_of(0, 0)) return;
     }
     int32_t slot_cur[KPT], slot_next[KPT];
-    slots_at(key0, slot_cur);
-    slots_at(key0 + kLgStage, slot_next);
+    slots_at(0, slot_cur);
+    slots_at(1, slot_next);
     __builtin_amdgcn_sched_barrier(0);   // keep the slot loads ahead of the query rows
 
     // this wavefront's tokens: gates (zero past H or T), then q rows (A
@@ -224,7 +245,7 @@ void mqa_logits_kernel(LogitsParams p) {
         // every load of the set-up has been issued.
         asm volatile("" : "+v"(lraw) :: "memory");
         kend = chunk_end();
-        if (kend <= key0) return;
+        if (kend <= key_of(0, 0)) return;
     }
 
     // stage loader: thread tid brings keys tid / 4 + 64 j (j < KPT) of a
@@ -236,13 +257,15 @@ void mqa_logits_kernel(LogitsParams p) {
     auto slot_ok = [&](int s, int32_t raw) {
         return s < kend && (!SLOTS || (uint32_t)raw < p.S);
     };
-    uint2 sreg[KPT][4];
-    float sscale[KPT];
-    int smask[KPT];
-    auto fetch = [&](int s0, const int32_t (&raw)[KPT]) {
+    struct StageRegs {
+        uint2 r[KPT][4];
+        float sc[KPT];
+        int m[KPT];
+    };
+    auto fetch = [&](StageRegs& R, int st, const int32_t (&raw)[KPT]) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const int s = s0 + 64 * j + sk;
+            const int s = key_of(st, 64 * j + sk);
             const bool ok = slot_ok(s, raw[j]);
             const uint32_t sl = ok ? (SLOTS ? (uint32_t)raw[j] : (uint32_t)s) : 0u;
             const uint8_t* row;
@@ -257,36 +280,35 @@ void mqa_logits_kernel(LogitsParams p) {
                 row = p.k_cache + (uint64_t)sl * (uint64_t)p.k_row_stride;
                 scl = p.k_scale + sl;
             }
-            smask[j] = lane_mask(ok);
+            R.m[j] = lane_mask(ok);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sreg[j][q] = *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * q);
-            sscale[j] = *scl;
+            for (int q = 0; q < 4; ++q) R.r[j][q] = *reinterpret_cast<const uint2*>(row + 32 * sp + 8 * q);
+            R.sc[j] = *scl;
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](const StageRegs& R, int buf) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             uint8_t* d = &kbuf[buf][(sk + 64 * j) * kLgRowPitch + 32 * sp];
-            const uint32_t m = (uint32_t)smask[j];
+            const uint32_t m = (uint32_t)R.m[j];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint2*>(d + 8 * q) = make_uint2(sreg[j][q].x & m, sreg[j][q].y & m);
-            if (sp == 0) kscl[buf][sk + 64 * j] = masked(sscale[j], smask[j]);
+                *reinterpret_cast<uint2*>(d + 8 * q) = make_uint2(R.r[j][q].x & m, R.r[j][q].y & m);
+            if (sp == 0) kscl[buf][sk + 64 * j] = masked(R.sc[j], R.m[j]);
         }
     };
 
     // output: after the reduction lanes 0..15 hold token 0's sums and (two
     // tokens) lanes 32..47 token 1's, for the 16 keys of a block (lane % 16);
-    // key offsets from here on are relative to key0 (below the chunk size,
-    // 32-bit)
+    // key offsets from here on are relative to key0 (32-bit)
     const int oi = TPW == 2 ? lane >> 5 : 0;
     const bool writer = TPW == 2 ? (lane & 16) == 0 : lane < 16;
     const int otok = t_wave + oi;
     const int olen = oi ? length_of(wave * kLgTokensPerWave + TPW - 1) : length_of(wave * kLgTokensPerWave);
     float* const obase = p.out + (int64_t)min(otok, p.T - 1) * p.out_stride + key0;
-    const int ostop = min(olen, kend) - key0;
+    const int wlen = min(olen, kend);       // one token per wavefront: its keys end here
+    const int ostop = wlen - key0;
     const int lim = writer && ostop > 0 ? ostop : 0;     // this lane stores keys rel < lim
-    const int nkeys = kend - key0;
 
     // ReLU, gate and head sum of one block's dots, then the sum over the four
     // lane groups: with two tokens, for both at once (the 32-lane swap pairs
@@ -313,61 +335,94 @@ void mqa_logits_kernel(LogitsParams p) {
         if (rel < lim) obase[rel] = v * ks;
     };
 
-    fetch(key0, slot_cur);
     int buf = 0;
     // One token per wavefront: each block's MFMAs are issued before the
-    // previous block's epilogue (its results held over in Cp), so the matrix
-    // unit works on one block while the VALU finishes the other, across the
-    // stage barriers too.  Two tokens run each block's MFMAs and epilogue in
-    // turn (their registers leave no room for a second set of results).
+    // previous block's epilogue (its results held over in Cp).  Two tokens
+    // run each block's MFMAs and epilogue in turn (their registers leave no
+    // room for a second set of results).
     v4f Cp[kLgTokensPerWave][kLgHeadBlocks];
     float ksp = 0.f;
     int relp = 0;
     bool havep = false;
+    // heads past H have zero rows and gates and keys past kend zero rows, so
+    // they add nothing
+    auto block_dots = [&](v4f (&C)[kLgTokensPerWave][kLgHeadBlocks], const v8i& B) {
+#pragma unroll
+        for (int i = 0; i < kLgTokensPerWave; ++i)
+#pragma unroll
+            for (int hb = 0; hb < kLgHeadBlocks; ++hb) C[i][hb] = dots16(A[i][hb], B);
+    };
+    if constexpr (TPW == 2) {
+        StageRegs R;
+        fetch(R, 0, slot_cur);
 #pragma unroll 1
-    for (int r0 = 0; r0 < nkeys; r0 += kLgStage, buf ^= 1) {
-        stash(buf);
-        __syncthreads();        // the stage is in LDS; every wavefront is done with the other buffer
-        if (r0 + kLgStage < nkeys) {
-            fetch(key0 + r0 + kLgStage, slot_next);
-            slots_at(key0 + r0 + 2 * kLgStage, slot_next);
-        }
-        // each block's key operand and scale are read from LDS one block ahead,
-        // so their latency hides behind the epilogue of the block before
-        constexpr bool kAhead = LgShape<TPW>::kReadAhead;
-        v8i Bn = load32(&kbuf[buf][(lane & 15) * kLgRowPitch + 32 * g]);
-        float ksn = kscl[buf][lane & 15];
-#pragma unroll
-        for (int kb = 0; kb < kLgStage / 16; ++kb) {
-            if (!kAhead && kb > 0) {
-                Bn = load32(&kbuf[buf][(kb * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
-                ksn = kscl[buf][kb * 16 + (lane & 15)];
+        for (int st = 0; key_of(st, 0) < kend; ++st, buf ^= 1) {
+            stash(R, buf);
+            __syncthreads();        // the stage is in LDS; every wavefront is done with the other buffer
+            if (key_of(st + 1, 0) < kend) {
+                fetch(R, st + 1, slot_next);
+                slots_at(st + 2, slot_next);
             }
-            const v8i B = Bn;
-            const float ks = ksn;
-            const int rel = r0 + kb * 16 + (lane & 15);
-            // heads past H have zero rows and gates and keys past kend zero
-            // rows, so they add nothing
-            v4f C[kLgTokensPerWave][kLgHeadBlocks];
+            // each block's key operand and scale are read from LDS one block
+            // ahead, so their latency hides behind the epilogue of the block
+            // before
+            v8i Bn = load32(&kbuf[buf][(lane & 15) * kLgRowPitch + 32 * g]);
+            float ksn = kscl[buf][lane & 15];
 #pragma unroll
-            for (int i = 0; i < kLgTokensPerWave; ++i)
-#pragma unroll
-                for (int hb = 0; hb < kLgHeadBlocks; ++hb) C[i][hb] = dots16(A[i][hb], B);
-            if (kAhead && kb + 1 < kLgStage / 16) {
-                Bn = load32(&kbuf[buf][((kb + 1) * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
-                ksn = kscl[buf][(kb + 1) * 16 + (lane & 15)];
-            }
-            if (TPW == 2) {
-                epilogue(C, ks, rel);
-            } else {
-                if (kb > 0 || havep) epilogue(Cp, ksp, relp);
-#pragma unroll
-                for (int hb = 0; hb < kLgHeadBlocks; ++hb) Cp[0][hb] = C[0][hb];
-                ksp = ks;
-                relp = rel;
+            for (int kb = 0; kb < kLgStage / 16; ++kb) {
+                const v8i B = Bn;
+                const float ks = ksn;
+                v4f C[kLgTokensPerWave][kLgHeadBlocks];
+                block_dots(C, B);
+                if (kb + 1 < kLgStage / 16) {
+                    Bn = load32(&kbuf[buf][((kb + 1) * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
+                    ksn = kscl[buf][(kb + 1) * 16 + (lane & 15)];
+                }
+                epilogue(C, ks, st * kLgStage + kb * 16 + (lane & 15));
             }
         }
-        havep = true;
+    } else {
+        // One resident round: the workgroup's two stages (its chunk of 256
+        // keys) are staged together behind one barrier, after which each
+        // wavefront runs through its own blocks with no further barrier and
+        // stops at its token's length.
+        {
+            StageRegs R0, R1;
+            fetch(R0, 0, slot_cur);
+            fetch(R1, 1, slot_next);
+            stash(R0, 0);
+            stash(R1, 1);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if (key_of(st, kLgStage - 16) < wlen) {
+#pragma unroll
+                for (int kb = 0; kb < kLgStage / 16; ++kb) {
+                    const v8i B = load32(&kbuf[st][(kb * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
+                    const float ks = kscl[st][kb * 16 + (lane & 15)];
+                    v4f C[kLgTokensPerWave][kLgHeadBlocks];
+                    block_dots(C, B);
+                    if (kb > 0 || havep) epilogue(Cp, ksp, relp);
+#pragma unroll
+                    for (int hb = 0; hb < kLgHeadBlocks; ++hb) Cp[0][hb] = C[0][hb];
+                    ksp = ks;
+                    relp = key_of(st, kb * 16) + (lane & 15);
+                }
+                havep = true;
+            } else if (key_of(st, 0) < wlen) {
+                if (havep) epilogue(Cp, ksp, relp);
+                havep = false;
+#pragma unroll 1
+                for (int kb = 0; kb < kLgStage / 16 && key_of(st, kb * 16) < wlen; ++kb) {
+                    const v8i B = load32(&kbuf[st][(kb * 16 + (lane & 15)) * kLgRowPitch + 32 * g]);
+                    const float ks = kscl[st][kb * 16 + (lane & 15)];
+                    v4f C[kLgTokensPerWave][kLgHeadBlocks];
+                    block_dots(C, B);
+                    epilogue(C, ks, key_of(st, kb * 16) + (lane & 15));
+                }
+            }
+        }
     }
     if (TPW == 1 && havep) epilogue(Cp, ksp, relp);
 }

@@ -645,6 +645,10 @@ void logits_calls() {
         for (const auto& l : g_launches) {
             const uint32_t d = l.lp.chunk_major ? (uint32_t)l.lp.blocks : (uint32_t)l.lp.chunks;
             CHECK(l.lp.blocks == (l.lp.T + 7) / 8);
+            // one token per wavefront: one resident round, and the workgroups'
+            // 16 strided key blocks cover every key
+            CHECK(l.lp.tokens_per_wave == ((int64_t)l.lp.blocks * l.lp.chunks <= 512 ? 1 : 2));
+            if (l.lp.tokens_per_wave == 1) CHECK((int64_t)l.lp.chunks * 256 >= l.lp.N);
             for (uint32_t b = 0; b < (uint32_t)l.lp.blocks * (uint32_t)l.lp.chunks; ++b)
                 CHECK((uint32_t)(((uint64_t)b * l.lp.grid_magic) >> l.lp.grid_shift) == b / d);
         }
