@@ -216,6 +216,38 @@ def test_epilogue_equals_key_entry_on_its_own_projection():
     assert np.array_equal(kc1, kc3) and np.array_equal(ks1.view(np.uint32), ks3.view(np.uint32))
 
 
+@pytest.mark.parametrize("x_st,w_st", [(448, 520), (1 << 22, 1 << 22)])
+def test_projection_strided_rows(x_st, w_st):
+    """Hidden and weight rows at strides above d, up to the largest the host
+    accepts (2^22 elements): the kernel's byte offsets within a workgroup's 256
+    rows then reach 255 * 2^23, just under 2^31.  The results equal those of
+    the contiguous call bit for bit (the same sums in the same order)."""
+    T, d, H = 300, 256, 24
+    pw = W.proj_make(T, d, H, seed=77, name="proj", table_rows=4096, num_slots=4096,
+                     slot_mode="perm_prefix")
+    ref = ProjCase(pw)
+    ref.run()
+    c = ProjCase(pw)
+    xbig = torch.zeros(((T - 1) * x_st + d,), dtype=torch.bfloat16, device="cuda")
+    wbig = torch.zeros(((ROW + H - 1) * w_st + d,), dtype=torch.bfloat16, device="cuda")
+    c.hidden = xbig.as_strided((T, d), (x_st, 1))
+    c.weight = wbig.as_strided((ROW + H, d), (w_st, 1))
+    c.hidden.copy_(ref.hidden)
+    c.weight.copy_(ref.weight)
+    print("\n[case] proj strided rows x_st=%d w_st=%d (%.1f GB of rows)" %
+          (x_st, w_st, (xbig.numel() + wbig.numel()) * 2 / 1e9), flush=True)
+    c.run()
+    assert np.array_equal(bits16(c.gates), bits16(ref.gates))
+    assert np.array_equal(bits16(c.k_out), bits16(ref.k_out))
+    kc, ks = c.cache_host()
+    kc0, ks0 = ref.cache_host()
+    assert np.array_equal(kc, kc0) and np.array_equal(ks.view(np.uint32), ks0.view(np.uint32))
+    rep = check_case(c)
+    del xbig, wbig, c
+    torch.cuda.empty_cache()
+    log("proj strided rows", rep)
+
+
 def test_projection_full_size_sampled():
     """The bench launch: 65536 tokens, d = 7168, H = 64, positions
     196608..262143, a 262144-slot cache.  The oracle runs on 2048 sampled
