@@ -51,9 +51,9 @@ constexpr int kLgHeadBlocks = kLogitsMaxHeads / 16;
 // Workgroup shape for TPW query tokens per wavefront: kLogitsTokensPerBlock
 // tokens per workgroup, so TPW = 2 is 4 wavefronts and TPW = 1 is 8; each
 // thread stages KPT key rows of a stage.  Register budgets: three wavefronts
-// per SIMD for two tokens (168 VGPRs); four for one (128 VGPRs: with the
-// pipelined blocks this leaves no room to read each key operand a block
-// ahead, so one token reads it just before its MFMAs).
+// per SIMD for two tokens (168 VGPRs); four for one (128 VGPRs, of which it
+// uses about 100; one token reads each key operand just before its MFMAs,
+// since reading it a block ahead measured no faster there).
 template <int TPW>
 struct LgShape {
     static_assert(TPW == 1 || TPW == 2, "one or two tokens per wavefront");
