@@ -105,7 +105,7 @@ def check(got, q8, w, codes, scale, key_slots=None, lengths=None, N=None):
 
 
 @pytest.mark.parametrize("T,H,S", [(64, 64, 4096), (41, 64, 1000), (9, 16, 300), (3, 1, 70),
-                                   (17, 33, 129), (8, 63, 64)])
+                                   (17, 33, 129), (8, 63, 64), (5, 64, 1), (33, 8, 15), (64, 64, 257)])
 def test_dense_keys(T, H, S):
     """One-token shape (grids of at most 512 workgroups)."""
     assert logits_grid(T, S) <= 512
